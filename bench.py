@@ -1,0 +1,199 @@
+"""Benchmark: routed FP16/INT8 causal prefill attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: blockwise INT8 quantisation of Q and K (and V for the
+INT8 KV cache), route-word packing, the varlen/GQA work list and the fused
+attention kernel.  Default workload: the LLaMA-3.2-3B-shaped attention layer
+(batch 8, L = 4096, 24 query / 8 KV heads, d = 128, causal, FP16, 4 outlier
+channels, 64x64 tiles, g = 1, 75 % of the legal tile groups INT8).
+
+Prints one JSON line (rank 0).  Extra fields: the attention kernel's own time
+and blended-MFMA roofline, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks
+P_FP16 = 2516.6e12        # FLOP/s
+P_INT8 = 5033.2e12        # OP/s
+HBM_PEAK = 8.0e12         # B/s
+
+
+def legal_pairs(lengths):
+    return sum(L * (L + 1) // 2 for L in lengths)
+
+
+def work_model(w, words):
+    """Algorithmic work of one attention call, split by route.
+
+    Per legal (query, key) pair: QK 2d ops on its tile's path, PV 2d fp16 flops.
+    Pairs are counted exactly per tile: full off-diagonal tiles, lower triangles
+    (clipped to the sequence) on the diagonal.  `words` are the packed route
+    words (uint64 [Hk][B][T]) the library built for this call."""
+    d = w.head_dim
+    G = w.num_q_heads // w.num_kv_heads
+    pairs16 = pairs8 = 0
+    for b, L in enumerate(w.lengths):
+        L = int(L)
+        Tb = (L + 63) // 64
+        for m in range(Tb):
+            rows = min(64, L - 64 * m)
+            for hk in range(w.num_kv_heads):
+                word = int(words[hk, b, m])
+                n_full = m                                   # key tiles 0..m-1 are fully legal
+                full8 = sum(((word >> (n // w.g)) & 1) for n in range(n_full))
+                diag = rows * (rows + 1) // 2
+                dbit = (word >> (m // w.g)) & 1
+                p8 = full8 * 64 * rows + (diag if dbit else 0)
+                p16 = (n_full - full8) * 64 * rows + (0 if dbit else diag)
+                pairs8 += G * p8
+                pairs16 += G * p16
+    f_qk16 = 2 * d * pairs16
+    f_qk8 = 2 * d * pairs8
+    f_pv = 2 * d * (pairs16 + pairs8)
+    t_star = f_qk16 / P_FP16 + f_qk8 / P_INT8 + f_pv / P_FP16
+    return dict(pairs=pairs16 + pairs8, pairs_int8=pairs8, f_qk16=f_qk16, f_qk8=f_qk8, f_pv=f_pv,
+                ops=f_qk16 + f_qk8 + f_pv, t_star=t_star)
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle (as it stands) on a bounded sample of the same workload,
+    extrapolated to the full step by legal-tile work."""
+    import oracle as orc
+    from tests.oracle_inputs import oracle_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    inp = oracle_inputs(w)          # quantise Q/K(/V) and pack the route words, in full
+    t_prep = time.perf_counter() - t0
+    spans = orc.seq_spans(w.cu_seqlens)
+    total_work = sum(w.num_q_heads * t * (t + 1) // 2 for t in (orc.num_tiles(L) for _, L in spans))
+    rng = np.random.default_rng(0)
+    done_work, t_attn, rows = 0, 0.0, 0
+    while t_attn < budget_s:
+        b = int(rng.integers(len(spans)))
+        Tb = orc.num_tiles(spans[b][1])
+        m = int(rng.integers(Tb))
+        hq = int(rng.integers(w.num_q_heads))
+        t1 = time.perf_counter()
+        orc.attn_tile_row(inp, b, hq, m)
+        t_attn += time.perf_counter() - t1
+        done_work += m + 1
+        rows += 1
+    t_full = t_prep + t_attn * total_work / done_work
+    return {"value": w.num_tokens / t_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"quantise+pack in full ({t_prep:.2f} s); attention on {rows} random (seq, head, query-tile) "
+                      f"rows ({done_work} of {total_work} legal tile visits, {t_attn:.1f} s), extrapolated by "
+                      f"legal-tile work"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--p", type=float, default=None, help="INT8 coverage override (configs 2, 4, 5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
+              "the sharding design is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixed_precision_amd import tilemix as tm
+    from workloads import config
+
+    dev = torch.device("cuda:0")
+    w = config(args.config, p=args.p)
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    tr = torch.from_numpy(w.tile_route).to(dev)
+    N, Hq, d = w.q.shape
+    Hk = w.num_kv_heads
+    B = w.batch
+    plan = tm.AttnPlan(tm.AttnProblem(B, w.max_seqlen, Hq, Hk, d, w.g, w.blk_q, w.sm_scale, w.kv_int8, False), dev)
+    nbq = (w.max_seqlen + w.blk_q - 1) // w.blk_q
+    T = w.T
+    q_q = torch.empty((N, Hq, d), dtype=torch.int8, device=dev)
+    q_s = torch.empty((Hq, B, nbq), dtype=torch.float32, device=dev)
+    k_q = torch.empty((N, Hk, d), dtype=torch.int8, device=dev)
+    k_s = torch.empty((Hk, B, T), dtype=torch.float32, device=dev)
+    v_q = torch.empty((N, Hk, d), dtype=torch.int8, device=dev) if w.kv_int8 else None
+    v_s = torch.empty((Hk, B, T), dtype=torch.float32, device=dev) if w.kv_int8 else None
+    words = torch.empty((Hk, B, T), dtype=torch.int64, device=dev)
+    out = torch.empty((N, Hq, d), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
+    work = work_model(w, words.cpu().numpy().view(np.uint64))
+
+    def step(ev=None):
+        tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
+        tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
+        if w.kv_int8:
+            tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
+        tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        if w.kv_int8:
+            plan.run(q, k_q, v_q, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream)
+        else:
+            plan.run(q, k, v, q_q, q_s, k_q, k_s, cu, words, out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    t_attn = float(np.mean(attn_ms)) * 1e-3
+    achieved = work["ops"] / t_attn
+    blended_peak = work["ops"] / work["t_star"]
+    tokens_per_s = N / (ms_per_step * 1e-3)
+
+    res = {
+        "metric": "prefill tokens/s & % blended MFMA peak, 3B-shaped GQA attn L=4K b=8 75% INT8",
+        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16+int8 (fp32 accumulation / int32 accumulation)", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": w.max_seqlen, "num_q_heads": Hq, "num_kv_heads": Hk,
+                   "head_dim": d, "g": w.g, "blk_q": w.blk_q, "kv_int8": w.kv_int8,
+                   "int8_pair_fraction": work["pairs_int8"] / work["pairs"], "tokens": N},
+        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / blended_peak, "traffic": None,
+                     "kernel": "attn_prefill_kernel (+ work-list kernels)",
+                     "note": "peak = blended MFMA peak of this launch's mix: ops / (F_qk16/P16 + F_qk8/P8 + F_pv/P16)"},
+        "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
+        "attn_tokens_per_s": N / t_attn, "t_star_ms": work["t_star"] * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

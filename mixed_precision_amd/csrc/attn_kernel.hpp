@@ -1,0 +1,526 @@
+// Fused causal routed FP16/INT8 prefill attention for gfx950 (MI355X).
+//
+// Method (paperlayer.ai summary of arXiv 2608.17336, "TileMix: Tile-Centric
+// Mixed-Precision Attention for LLM Inference Acceleration": §1, §3
+// Preliminaries, §4, App. C; ainews.surl.tw article on TileMix): for each query
+// tile the legal key tiles are streamed; a bit of the row's packed 64-bit word,
+// (w >> floor(n/g)) & 1, sends tile n through an FP16 or an INT8 QK^T (INT32
+// accumulation, then the block scales); both update one online-softmax state
+// (running max, sum, output accumulator) and P.V runs in FP16.
+//
+// gfx950 design (the pages' A100/Triton kernel is prior art, not followed):
+//  * Workgroup = 4 wavefronts = one work item (sequence b, KV head hk, query
+//    tile m, up to 3 of the query heads that share hk); two workgroups share a
+//    CU (2 waves per SIMD) so one wave's softmax overlaps the other's MFMAs.
+//    All of the item's query heads take the same route bit and read the same
+//    K/V tiles, so one LDS copy of each tile feeds 4*nh query blocks of 16
+//    rows; wave w owns nh of them (nh = heads in the chunk), which balances
+//    GQA ratios such as 3 over the 4 SIMDs.
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_f16
+//    or v_mfma_i32_16x16x64_i8: A = K rows from LDS, B = Q^T from registers
+//    (loaded once per item).  In the 16x16 accumulator layout each lane then
+//    holds one query column and a quarter of the keys, so the softmax
+//    statistics need one max over 4 lanes, and the exponentials are already
+//    laid out as the B operand (P^T) of the P.V MFMA: O^T += V^T P^T.  The A
+//    operand V^T comes straight from V's natural [key][d] layout through
+//    ds_read_b64_tr_b16 (within each 16-lane group the 16x4 block of b16 the
+//    lanes address is handed back transposed).  O^T has one query per lane,
+//    so the rescale and the final 1/l are lane-local.
+//  * Tiles are processed in 32-key halves (QK, softmax, P.V per half) to keep
+//    the live score registers small; the online softmax is exact at any
+//    granularity.
+//  * The route bit is wave-uniform (SGPR shift and mask), so the FP16/INT8
+//    choice is a scalar branch around the QK^T only; one loop body serves every
+//    tile (duplicating it per route costs the register allocator dearly).
+//  * FP16 K/V tiles move HBM -> LDS with buffer_load ... lds (no staging
+//    registers); the next tile's loads are in flight while the current tile
+//    computes from the other half of a double-buffered stage.  K is fetched
+//    in the form its route needs (fp16 16 KB or int8 8 KB at d = 128).  An
+//    INT8 KV cache goes through registers, widened int8 -> fp16 exactly where
+//    the FP16 path or P.V needs it.  Buffer range checks return zeros past the
+//    sequence end, so ragged tails need no branches.
+//  * Scores live in the log2 domain: t = raw * c with c = sm_scale*log2(e)
+//    (FP16 path) or q_scale*k_scale*sm_scale*log2(e) (INT8 path), so both paths
+//    meet in one running max and p = exp2(raw*c - m) is one FMA plus v_exp_f32.
+//    The reference max only moves when a half-tile's max exceeds it by more
+//    than kSlack, so the accumulator is rescaled on few tiles; acc / l is
+//    unchanged.  Raw scores are held in integer-typed registers (INT8 results
+//    as int32, FP16 results as their float bits) so no float transformation
+//    ever touches an int32 bit pattern.
+//  * With an fp16 V the normaliser l sums the fp16-rounded probabilities that
+//    actually enter P.V (v_dot2_f32_f16), so O is an exact weighted mean of V
+//    rows with slightly perturbed weights and the dominant term's rounding
+//    cancels.
+#pragma once
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace tilemix {
+
+constexpr float kSlack = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+TM_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+TM_DEV u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// 16 bytes per lane from global straight into LDS at lds_base + lane*16.
+TM_DEV void bload16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, 0);
+}
+TM_DEV f16x4 read_tr16(const char* p) {
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+TM_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
+
+template <int D, int QB, bool KVI8>
+struct Attn {
+  static constexpr int NDS = D / 32;       // fp16 MFMA k-steps over d
+  static constexpr int NDS8 = D / 64;      // int8 MFMA k-steps over d
+  static constexpr int NDB = D / 16;       // 16-row blocks of d in O^T
+  static constexpr int RB16 = 2 * D;       // bytes of one fp16 row (K or V)
+  static constexpr int RB8 = D;            // bytes of one int8 K row
+  // LDS tile layout: a tile's 64 rows are spread over NB = 64 / (1024/RB)
+  // blocks of 1 KB (padded to 1040 B); row r sits in block r % NB at slot
+  // r / NB.  The 16 consecutive rows one MFMA operand read touches then fall in
+  // 16 different 16-byte bank groups, every operand address is a per-lane base
+  // plus an immediate, and one lds-load instruction fills one whole block.
+  static constexpr int BLK = 1040;
+  template <int RB>
+  struct Lay {
+    static constexpr int NB = 64 / (1024 / RB);
+    static TM_DEV int row(int r) { return (r % NB) * BLK + (r / NB) * RB; }
+    // row 16*k + c16 (c16 < 16): per-lane part and compile-time part
+    static TM_DEV int lane(int c16) { return (c16 % NB) * BLK + (c16 / NB) * RB; }
+    static constexpr int step16 = (16 / NB) * RB;
+  };
+  using L16 = Lay<RB16>;
+  using L8 = Lay<RB8>;
+  static constexpr int TBYTES = L16::NB * BLK;             // one fp16 tile (int8 uses half)
+  static constexpr int LDS_BYTES = 4 * TBYTES;             // K and V, double-buffered
+  static constexpr int NI16 = L16::NB / 4;                 // lds-load instructions per wave, fp16 tile
+  static constexpr int NI8 = L8::NB / 4;                   // ... int8 tile
+
+  static TM_DEV int k16_off(int R, int C) { return L16::row(R) + C * 16; }
+  static TM_DEV int k8_off(int R, int C) { return L8::row(R) + C * 16; }
+  static TM_DEV int v_off(int key, int d) { return L16::row(key) + d * 2; }
+
+  // Per-lane global byte offsets (relative to the tile's first row) of the
+  // lds-loads; instruction i of wave w fills block w*NI + i.
+  struct Dma {
+    uint32_t k16[NI16], v[NI16], k8[NI8];
+  };
+  static TM_DEV void dma_offsets(Dma& o, int wave, int lane, uint32_t k16_stride, uint32_t k8_stride,
+                                 uint32_t v_stride) {
+#pragma unroll
+    for (int i = 0; i < NI16; ++i) {
+      const int q = wave * NI16 + i;
+      const int R = q + L16::NB * ((lane * 16) / RB16), p = ((lane * 16) % RB16) / 16;
+      o.k16[i] = R * k16_stride + p * 16;
+      o.v[i] = R * v_stride + p * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < NI8; ++i) {
+      const int q = wave * NI8 + i;
+      const int R = q + L8::NB * ((lane * 16) / RB8), p = ((lane * 16) % RB8) / 16;
+      o.k8[i] = R * k8_stride + p * 16;
+    }
+  }
+
+  // --- FP16 KV: issue the lds-loads of tile n (K in its route's form, and V)
+  static TM_DEV void dma_tile(int route, int wave, const Dma& o, __amdgpu_buffer_rsrc_t rk16,
+                              __amdgpu_buffer_rsrc_t rk8, __amdgpu_buffer_rsrc_t rv, char* kl, char* vl) {
+    if (route == 0) {
+#pragma unroll
+      for (int i = 0; i < NI16; ++i) bload16_lds(rk16, o.k16[i], kl + (wave * NI16 + i) * BLK);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI8; ++i) bload16_lds(rk8, o.k8[i], kl + (wave * NI8 + i) * BLK);
+    }
+#pragma unroll
+    for (int i = 0; i < NI16; ++i) bload16_lds(rv, o.v[i], vl + (wave * NI16 + i) * BLK);
+  }
+
+  // --- INT8 KV cache: register staging (16 int8 of one row per thread and load)
+  struct Stage {
+    u32x4 k[D / 64];   // K: 64 x D bytes = D/64 loads of 16 B per thread
+    u32x4 v[D / 64];
+  };
+  static TM_DEV void stage_load(Stage& r, int tid, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                uint32_t stride) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const int id = tid + 256 * i;
+      const uint32_t off = (id / (D / 16)) * stride + (id % (D / 16)) * 16;
+      r.k[i] = bload16(rk, off);
+      r.v[i] = bload16(rv, off);
+    }
+  }
+  static TM_DEV void stage_store(const Stage& r, int route, int tid, char* kl, char* vl) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const int id = tid + 256 * i;
+      const int R = id / (D / 16), col = id % (D / 16);   // 16 int8 channels: col*16 ..
+      u32x4 c0, c1;
+      if (route == 1) {
+        *reinterpret_cast<u32x4*>(kl + k8_off(R, col)) = r.k[i];
+      } else {
+        i8x16_to_f16x16(r.k[i], c0, c1);
+        *reinterpret_cast<u32x4*>(kl + k16_off(R, 2 * col)) = c0;
+        *reinterpret_cast<u32x4*>(kl + k16_off(R, 2 * col + 1)) = c1;
+      }
+      i8x16_to_f16x16(r.v[i], c0, c1);
+      *reinterpret_cast<u32x4*>(vl + v_off(R, col * 16)) = c0;
+      *reinterpret_cast<u32x4*>(vl + v_off(R, col * 16 + 8)) = c1;
+    }
+  }
+
+  // --- raw S^T for the 32-key half h: FP16 path (float bits in int registers)
+  static TM_DEV void qk16(const char* kl, int h, const f16x8 (&qf)[QB][NDS], i32x4 (&S)[QB][2], int c, int gq) {
+    f32x4 acc[QB][2];
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc[j][kk] = f32x4{0, 0, 0, 0};
+    const char* base = kl + L16::lane(c) + gq * 16;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const f16x8 ak = *reinterpret_cast<const f16x8*>(base + (2 * h + kk) * L16::step16 + ds * 64);
+#pragma unroll
+        for (int j = 0; j < QB; ++j)
+          acc[j][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qf[j][ds], acc[j][kk], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) S[j][kk] = __builtin_bit_cast(i32x4, acc[j][kk]);
+  }
+
+  // --- raw S^T for the 32-key half h: INT8 path (exact int32 accumulation)
+  static TM_DEV void qk8(const char* kl, int h, const i32x4 (&q8)[QB][NDS8], i32x4 (&S)[QB][2], int c, int gq) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) S[j][kk] = i32x4{0, 0, 0, 0};
+    const char* base = kl + L8::lane(c) + gq * 16;
+#pragma unroll
+    for (int ds = 0; ds < NDS8; ++ds) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const i32x4 ak = *reinterpret_cast<const i32x4*>(base + (2 * h + kk) * L8::step16 + ds * 64);
+#pragma unroll
+        for (int j = 0; j < QB; ++j)
+          S[j][kk] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ak, q8[j][ds], S[j][kk], 0, 0, 0);
+      }
+    }
+  }
+
+  // --- INT8 results -> float bits, in place (the registers stay int-typed)
+  static TM_DEV void int_to_float_bits(i32x4 (&S)[QB][2]) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) S[j][kk] = __builtin_bit_cast(i32x4, __builtin_convertvector(S[j][kk], f32x4));
+  }
+
+  // --- diagonal tile: key offset must not exceed query offset
+  static TM_DEV void mask_diag(i32x4 (&S)[QB][2], int h, const int (&qrow)[QB], int gq) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (32 * h + 16 * kk + gq * 4 + i > qrow[j]) S[j][kk][i] = __builtin_bit_cast(int32_t, -INFINITY);
+  }
+
+  // --- shared online-softmax update for half h from raw scores (float bits).
+  // Returns true in lanes whose reference max moved (alpha < 1).
+  static TM_DEV bool softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float vsc, float (&mref)[QB],
+                             float (&lrow)[QB], float (&alpha)[QB], f16x8 (&P)[QB]) {
+    bool moved = false;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      // Whole-vector bit casts: clang mis-lowers __builtin_bit_cast applied to
+      // a single element of an ext_vector (it reads element 0).
+      float x[2][4];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const f32x4 xv = __builtin_bit_cast(f32x4, S[j][kk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[kk][i] = xv[i];
+      }
+      float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float tmax = mx * cj[j];
+      const float mnew = (tmax > mref[j] + kSlack) ? tmax : mref[j];
+      alpha[j] = __builtin_amdgcn_exp2f(mref[j] - mnew);
+      moved |= (mnew != mref[j]);
+      mref[j] = mnew;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kk][i], cj[j], -mnew));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kk][i + 1], cj[j], -mnew));
+          f16x2 hv;
+          if (KVI8) {
+            hv = f16x2{(f16)(p0 * vsc), (f16)(p1 * vsc)};
+            lsum += p0 + p1;
+          } else {
+            hv = f16x2{(f16)p0, (f16)p1};
+            lsum = __builtin_amdgcn_fdot2(hv, f16x2{(f16)1.0f, (f16)1.0f}, lsum, false);
+          }
+          P[j][kk * 4 + i] = hv[0];
+          P[j][kk * 4 + i + 1] = hv[1];
+        }
+      }
+      lrow[j] = lrow[j] * alpha[j] + lsum;
+    }
+    return moved;
+  }
+
+  // --- O^T += V^T P^T for half h.  Lane (c, gq) needs, for channel db*16+c,
+  // keys 32h+4gq+0..3 (lo) and 32h+16+4gq+0..3 (hi); each comes from one
+  // ds_read_b64_tr_b16 whose 16 lanes address 4 keys x 16 channels.
+  static TM_DEV void pv(const char* vl, int h, const f16x8 (&P)[QB], f32x4 (&O)[QB][NDB], int lane) {
+    const int gq = lane >> 4, jl = lane & 15;
+    // key 32h + 16e + (4gq + jl/4), channels db*16 + 4*(jl%4) .. +3
+    const char* base = vl + L16::lane(4 * gq + (jl >> 2)) + 8 * (jl & 3);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const f16x4 lo = read_tr16(base + (2 * h) * L16::step16 + db * 32);
+      const f16x4 hi = read_tr16(base + (2 * h + 1) * L16::step16 + db * 32);
+      const f16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int j = 0; j < QB; ++j) O[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, P[j], O[j][db], 0, 0, 0);
+    }
+  }
+};
+
+template <int D, int QB, bool KVI8, bool DBG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_prefill_kernel(const AttnArgs a) {
+  using A = Attn<D, QB, KVI8>;
+  constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
+  __shared__ __attribute__((aligned(1024))) char smem[A::LDS_BYTES];
+  auto kbuf = [&](int i) -> char* { return smem + i * A::TBYTES; };                   // i in 0..1
+  auto vbuf = [&](int i) -> char* { return smem + (2 + i) * A::TBYTES; };             // i in 0..1
+
+  const WorkItem item = a.items[blockIdx.x];
+  const int b = uniform(item.b);
+  if (b < 0) return;
+  const int hk = uniform(item.hk);
+  const int m = uniform(item.m);
+  const int chunk = uniform(item.chunk);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = lane & 15;           // query column / operand row inside a 16-block
+  const int gq = lane >> 4;          // lane group 0..3
+  const int seq0 = uniform(a.cu[b]);
+  const int L = uniform(a.cu[b + 1]) - seq0;
+  const int h_begin = chunk * a.hc;
+  const int nh = min(a.hc, a.G - h_begin);   // heads in this chunk = q-blocks per wave
+
+  // ---- per q-block bookkeeping (recomputed where needed, not kept live)
+  auto qb_rb = [&](int j) { return (wave * nh + j) & 3; };                          // row block in tile
+  auto qb_head = [&](int j) { return hk * a.G + h_begin + ((wave * nh + j) >> 2); };
+  auto qb_row = [&](int j) { return qb_rb(j) * 16 + c; };                           // query offset in tile
+  auto qb_valid = [&](int j) { return (j < nh) && (m * kTile + qb_row(j) < L); };
+  float sq[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int blk_start = m * kTile + qb_rb(j) * 16;
+    sq[j] = 1.0f;
+    if (j < nh && blk_start < L)
+      sq[j] = a.q_scale[((int64_t)qb_head(j) * a.batch + b) * a.nbq + blk_start / a.blk_q];
+  }
+
+  // ---- Q operands (B = Q^T): fp16 and int8, loaded once
+  f16x8 qf[QB][NDS];
+  i32x4 q8[QB][NDS8];
+  const f16* qptr = static_cast<const f16*>(a.q);
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int64_t tok = (int64_t)seq0 + m * kTile + qb_row(j);
+    const bool valid = qb_valid(j);
+    const int hqj = qb_head(j);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+      qf[j][ds] = valid ? *reinterpret_cast<const f16x8*>(qptr + tok * a.q_st + (int64_t)hqj * a.q_sh + ds * 32 +
+                                                         gq * 8)
+                        : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int ds = 0; ds < NDS8; ++ds)
+      q8[j][ds] = valid ? *reinterpret_cast<const i32x4*>(a.q_q + (tok * a.Hq + hqj) * D + ds * 64 + gq * 16)
+                        : i32x4{0, 0, 0, 0};
+  }
+
+  // ---- sources: this sequence's rows of KV head hk.  Per tile the buffer
+  // base moves to the tile's first row and the range shrinks to the rows left,
+  // so rows >= L read as zero.
+  const int64_t esz = KVI8 ? 1 : 2;
+  const char* kbase = static_cast<const char*>(a.k) + ((int64_t)seq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
+  const char* vbase = static_cast<const char*>(a.v) + ((int64_t)seq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
+  const uint32_t kv_stride = (uint32_t)(a.kv_st * esz);
+  const uint32_t k8_stride = KVI8 ? kv_stride : (uint32_t)(a.Hk * D);
+  const char* k8base = KVI8 ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)seq0 * a.Hk + hk) * D);
+  auto tile_rsrc = [&](const char* base, uint32_t stride, int n) {
+    const int rows = max(L - n * kTile, 0);
+    return make_rsrc(base + (int64_t)n * kTile * stride, (uint32_t)rows * stride);
+  };
+  typename A::Dma dma;
+  if (!KVI8) A::dma_offsets(dma, wave, lane, kv_stride, k8_stride, kv_stride);
+
+  const uint64_t word = uniform64(a.words[((int64_t)hk * a.batch + b) * a.T + m]);
+  const int g = a.g;
+  const float* kscale_row = a.k_scale + ((int64_t)hk * a.batch + b) * a.T;
+  const float* vscale_row = KVI8 ? a.v_scale + ((int64_t)hk * a.batch + b) * a.T : nullptr;
+  auto route_of = [&](int n) -> int {
+    const int grp = n / g;
+    return grp < 64 ? (int)((word >> grp) & 1ull) : 0;
+  };
+  auto fetch = [&](int n, typename A::Stage& st) {     // start the loads of tile n
+    if (KVI8) {
+      A::stage_load(st, tid, tile_rsrc(kbase, kv_stride, n), tile_rsrc(vbase, kv_stride, n), kv_stride);
+    } else {
+      A::dma_tile(route_of(n), wave, dma, tile_rsrc(kbase, kv_stride, n), tile_rsrc(k8base, k8_stride, n),
+                  tile_rsrc(vbase, kv_stride, n), kbuf(n & 1), vbuf(n & 1));
+    }
+  };
+
+  // ---- online-softmax state (log2 domain), output accumulator O^T
+  f32x4 O[QB][NDB];
+  float mref[QB], lrow[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    mref[j] = -INFINITY;
+    lrow[j] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) O[j][db] = f32x4{0, 0, 0, 0};
+  }
+
+  // ---- prologue: tile 0 into stage 0
+  {
+    typename A::Stage st;
+    fetch(0, st);
+    if (KVI8) A::stage_store(st, route_of(0), tid, kbuf(0), vbuf(0));
+  }
+  wait_vmem();
+  __syncthreads();
+
+  // Tile n: tile n+1's loads are issued first (into stage (n+1)%2, last read
+  // in step n-1), then tile n is computed from stage n%2 in two 32-key halves.
+  // One loop body serves every tile; only the QK^T path and the diagonal mask
+  // branch (uniformly) inside it.
+  for (int n = 0; n <= m; ++n) {
+    const int rc = route_of(n);
+    const bool last = (n == m);
+    const char* kl = kbuf(n & 1);
+    const char* vl = vbuf(n & 1);
+    typename A::Stage st;
+    if (!last) fetch(n + 1, st);
+    const float ksc = kscale_row[n];
+    float cj[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) cj[j] = rc ? sq[j] * ksc * a.sm_log2 : (KVI8 ? ksc * a.sm_log2 : a.sm_log2);
+    const float vsc = KVI8 ? vscale_row[n] : 1.0f;
+    if (DBG) {
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const int qbi = wave * nh + j;
+        if (j < nh && (qbi & 3) == 0 && lane == 0) {
+          const int64_t t = (((int64_t)b * a.Hq + qb_head(j)) * a.T + m) * a.T + n;
+          if (a.dbg_visits) atomicAdd(a.dbg_visits + t, 1u);
+          if (a.dbg_route) a.dbg_route[t] = (uint8_t)rc;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      i32x4 S[QB][2];
+      if (rc == 0) {
+        A::qk16(kl, h, qf, S, c, gq);
+      } else {
+        A::qk8(kl, h, q8, S, c, gq);
+        if (DBG) {
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            if (j < nh && b == a.dbg_seq && qb_head(j) == a.dbg_head && m >= a.dbg_m0 && m < a.dbg_m1 && a.dbg_s32) {
+              int32_t* dst = a.dbg_s32 + ((((int64_t)(m - a.dbg_m0) * a.T + n) * kTile + qb_row(j)) * kTile);
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk)
+                *reinterpret_cast<i32x4*>(dst + (2 * h + kk) * 16 + gq * 4) = S[j][kk];
+            }
+          }
+        }
+        A::int_to_float_bits(S);
+      }
+      if (last) {
+        int qrow[QB];
+#pragma unroll
+        for (int j = 0; j < QB; ++j) qrow[j] = qb_row(j);
+        A::mask_diag(S, h, qrow, gq);
+      }
+      f16x8 P[QB];
+      float alpha[QB];
+      const bool moved = A::softmax(S, cj, vsc, mref, lrow, alpha, P);
+      if (__any(moved)) {
+#pragma unroll
+        for (int j = 0; j < QB; ++j)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) O[j][db] *= alpha[j];
+      }
+      A::pv(vl, h, P, O, lane);
+    }
+    if (!last) {
+      if (KVI8) A::stage_store(st, route_of(n + 1), tid, kbuf((n + 1) & 1), vbuf((n + 1) & 1));
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: O = acc / l
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    if (j >= nh) continue;
+    float l = lrow[j];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = 1.0f / l;
+    if (!qb_valid(j)) continue;
+    const int64_t tok = (int64_t)seq0 + m * kTile + qb_row(j);
+    const int64_t base = (tok * a.Hq + qb_head(j)) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const f32x4 r = O[j][db] * inv;
+      if (a.out_fp32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + base + db * 16 + gq * 4) = r;
+      } else {
+        f16x4 hv = {(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
+        *reinterpret_cast<f16x4*>(static_cast<f16*>(a.out) + base + db * 16 + gq * 4) = hv;
+      }
+    }
+  }
+}
+
+template <int D, int QB, bool KVI8, bool DBG>
+hipError_t launch_attn_inst(const AttnArgs& a, int64_t nslots, hipStream_t s) {
+  hipLaunchKernelGGL((attn_prefill_kernel<D, QB, KVI8, DBG>), dim3((unsigned)nslots), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tilemix

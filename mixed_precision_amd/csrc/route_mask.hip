@@ -1,0 +1,73 @@
+// Route-word packer and decoder.
+//
+// One 64-bit word per (KV head, sequence, query-tile row); bit j covers key
+// tiles [j*g, j*g+g), least significant bit first, 1 = INT8 path.  Decoding is
+// the constant-time shift-and-mask R = (w >> floor(n/g)) & 1.  (paperlayer.ai
+// summary of arXiv 2608.17336, "TileMix: Tile-Centric Mixed-Precision Attention
+// for LLM Inference Acceleration", §3 Preliminaries, §4 and App. D; gist.science
+// technical summary, compact-bitmask routing.)
+//
+// The packer takes per-tile decisions; a group's bit is the AND of its legal
+// tiles (FP16 wins on disagreement) and bits of groups without a legal tile are
+// 0, so equal decisions give equal words.  Both kernels are tiny (one thread
+// per word or per tile) and run once per routing template.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace tilemix {
+
+__global__ __launch_bounds__(256) void build_route_kernel(RouteArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.num_kv_heads * a.batch * a.T;
+  if (idx >= total) return;
+  const int m = (int)(idx % a.T);
+  const int b = (int)((idx / a.T) % a.batch);
+  const int L = a.cu[b + 1] - a.cu[b];
+  const int Tb = (L + kTile - 1) / kTile;
+  uint64_t w = 0;
+  if (m < Tb) {
+    const uint8_t* row = a.tile_route + idx * a.T;   // [hk][b][m][:]
+    bool all = true;
+    for (int n = 0; n <= m; ++n) {
+      all = all && (row[n] != 0);
+      if ((n + 1) % a.g == 0 || n == m) {
+        if (all) w |= 1ull << (n / a.g);
+        all = true;
+      }
+    }
+  }
+  a.words_out[idx] = w;
+}
+
+__global__ __launch_bounds__(256) void decode_route_kernel(RouteArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.num_kv_heads * a.batch * a.T * a.T;
+  if (idx >= total) return;
+  const int n = (int)(idx % a.T);
+  const int64_t wi = idx / a.T;                  // [hk][b][m]
+  const int m = (int)(wi % a.T);
+  const int b = (int)((wi / a.T) % a.batch);
+  const int L = a.cu[b + 1] - a.cu[b];
+  const int Tb = (L + kTile - 1) / kTile;
+  uint8_t out = 0xFF;
+  if (n <= m && m < Tb) out = (uint8_t)((a.words_in[wi] >> (n / a.g)) & 1ull);
+  a.tile_route_out[idx] = out;
+}
+
+hipError_t launch_build_route(const RouteArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.num_kv_heads * a.batch * a.T;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(build_route_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.num_kv_heads * a.batch * a.T * a.T;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_route_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tilemix

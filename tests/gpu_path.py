@@ -1,0 +1,64 @@
+"""Run a synthetic workload through the HIP library (via the binding) on cuda:0.
+
+Every operand the attention call consumes is produced by the library itself
+(quantiser, route packer); the oracle side builds its own from the same host
+arrays, so the two share only the seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from mixed_precision_amd import tilemix as tm
+from workloads import Workload
+
+DEV = "cuda:0"
+
+
+def upload(w: Workload, dev=DEV):
+    return dict(q=torch.from_numpy(w.q).to(dev), k=torch.from_numpy(w.k).to(dev), v=torch.from_numpy(w.v).to(dev),
+                cu=torch.from_numpy(w.cu_seqlens).to(dev), tile_route=torch.from_numpy(w.tile_route).to(dev))
+
+
+def prepare(w: Workload, dev=DEV, t=None):
+    """Device tensors for one attention call, operands made by the library."""
+    t = t or upload(w, dev)
+    t["q_q"], t["q_s"] = tm.tilemix_quantize_blockwise(t["q"], t["cu"], w.max_seqlen, w.blk_q)
+    if w.kv_int8:
+        t["k8"], t["k_s"] = tm.tilemix_quantize_blockwise(t["k"], t["cu"], w.max_seqlen, 64)
+        t["v8"], t["v_s"] = tm.tilemix_quantize_blockwise(t["v"], t["cu"], w.max_seqlen, 64)
+        t["k_q"] = None
+    else:
+        t["k_q"], t["k_s"] = tm.tilemix_quantize_blockwise(t["k"], t["cu"], w.max_seqlen, 64)
+    t["words"] = tm.tilemix_build_route_mask(t["tile_route"], t["cu"], w.max_seqlen, w.g)
+    return t
+
+
+def attn(w: Workload, t, out_fp32=True, plan=None, out=None):
+    if w.kv_int8:
+        return tm.tilemix_attn_prefill(t["q"], t["k8"], t["v8"], q_q=t["q_q"], q_scale=t["q_s"], k_q=None,
+                                       k_scale=t["k_s"], v_scale=t["v_s"], kv_int8=True, cu_seqlens=t["cu"],
+                                       route_words=t["words"], max_seqlen=w.max_seqlen, g=w.g, blk_q=w.blk_q,
+                                       sm_scale=w.sm_scale, out_fp32=out_fp32, plan=plan, out=out)
+    return tm.tilemix_attn_prefill(t["q"], t["k"], t["v"], q_q=t["q_q"], q_scale=t["q_s"], k_q=t["k_q"],
+                                   k_scale=t["k_s"], cu_seqlens=t["cu"], route_words=t["words"],
+                                   max_seqlen=w.max_seqlen, g=w.g, blk_q=w.blk_q, sm_scale=w.sm_scale,
+                                   out_fp32=out_fp32, plan=plan, out=out)
+
+
+def attn_debug(w: Workload, t, seq=0, q_head=0, m_begin=0, m_end=None):
+    kw = dict(q_q=t["q_q"], q_scale=t["q_s"], k_scale=t["k_s"], cu_seqlens=t["cu"], route_words=t["words"],
+              max_seqlen=w.max_seqlen, g=w.g, blk_q=w.blk_q, sm_scale=w.sm_scale, seq=seq, q_head=q_head,
+              m_begin=m_begin, m_end=m_end)
+    if w.kv_int8:
+        return tm.tilemix_attn_prefill_debug(t["q"], t["k8"], t["v8"], k_q=None, v_scale=t["v_s"], kv_int8=True, **kw)
+    return tm.tilemix_attn_prefill_debug(t["q"], t["k"], t["v"], k_q=t["k_q"], **kw)
+
+
+def words_u64(words: torch.Tensor) -> np.ndarray:
+    return words.cpu().numpy().view(np.uint64)
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    got = got.astype(np.float64)
+    diff = got - ref
+    return float(np.max(np.abs(diff))), float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))

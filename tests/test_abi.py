@@ -1,0 +1,114 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header
+declares, and rejects invalid arguments on the host before any launch (no
+compute call is made here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tilemix.h")
+LIB = os.path.join(ROOT, "mixed_precision_amd", "libtilemix.so")
+
+
+@pytest.fixture(scope="module")
+def tm():
+    if not os.path.exists(LIB):
+        from mixed_precision_amd import build as b
+        b.build(verbose=False)
+    from mixed_precision_amd import tilemix
+    return tilemix
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tilemix_\w+)\s*\(", src)))
+
+
+def test_header_declares_expected_calls():
+    names = header_functions()
+    for n in ("tilemix_quantize_blockwise", "tilemix_build_route_mask", "tilemix_decode_route_mask",
+              "tilemix_attn_workspace_size", "tilemix_attn_prefill", "tilemix_attn_prefill_debug",
+              "tilemix_status_string", "tilemix_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(tm):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (tilemix_\w+)", out))
+    declared = set(header_functions())
+    assert declared <= exported, declared - exported
+    assert set(tm.EXPORTED) == declared
+    for n in declared:
+        getattr(tm.lib(), n)
+
+
+def test_status_strings(tm):
+    for code, name in tm.STATUS_NAMES.items():
+        assert tm.lib().tilemix_status_string(code).decode() == name
+    assert tm.lib().tilemix_version().decode().startswith("tilemix")
+
+
+def _params(tm, **kw):
+    base = dict(batch=8, max_seqlen=4096, num_q_heads=24, num_kv_heads=8, head_dim=128, g=1, blk_q=64,
+                sm_scale=0.088388, kv_int8=False, out_fp32=False)
+    base.update(kw)
+    return tm.AttnProblem(**base)
+
+
+def test_workspace_size_and_param_validation(tm):
+    n = tm.tilemix_attn_workspace_size(_params(tm))
+    # work list: 8 x 64 x 8 items of 16 bytes, plus the segment table
+    assert n >= 8 * 64 * 8 * 16 and n % 256 == 0
+    bad = [
+        (dict(head_dim=96), 2), (dict(blk_q=32), 2), (dict(num_q_heads=20), 1), (dict(num_kv_heads=0), 1),
+        (dict(batch=0), 1), (dict(max_seqlen=0), 1), (dict(g=0), 1), (dict(max_seqlen=64 * 65, g=1), 3),
+        (dict(sm_scale=0.0), 1), (dict(sm_scale=float("nan")), 1),
+    ]
+    for kw, status in bad:
+        with pytest.raises(tm.TilemixError) as e:
+            tm.tilemix_attn_workspace_size(_params(tm, **kw))
+        assert e.value.status == status, (kw, e.value)
+    assert tm.tilemix_attn_workspace_size(_params(tm, max_seqlen=64 * 65, g=2)) > 0
+
+
+def test_null_pointer_and_workspace_errors(tm):
+    lib = tm.lib()
+    p = _params(tm).params()
+    t = tm.AttnTensors()
+    st = lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None)
+    assert st == 1 and "non-NULL" in tm.last_error()
+    # well-formed (fake, 256-aligned) addresses but no workspace: rejected before any launch
+    a = 1 << 20
+    t = tm.AttnTensors(a, a, a, 24 * 128, 128, 8 * 128, 128, a, a, a, a, None, a, a, a)
+    st = lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None)
+    assert st == 4 and "workspace" in tm.last_error()
+    t.q_stride_tok = 24 * 128 + 3
+    st = lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None)
+    assert st == 1 and "stride" in tm.last_error()
+    pc = _params(tm).params()
+    pc.causal = 0
+    t.q_stride_tok = 24 * 128
+    assert lib.tilemix_attn_prefill(ctypes.byref(pc), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 2
+    assert lib.tilemix_attn_prefill_debug(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None,
+                                          None) == 1
+
+
+def test_quantize_and_route_validation(tm):
+    lib = tm.lib()
+    a = ctypes.c_void_p(1 << 20)
+    assert lib.tilemix_quantize_blockwise(None, 128, 128, a, 1, 64, 1, 128, 64, a, a, None) == 1
+    assert lib.tilemix_quantize_blockwise(a, 128, 128, a, 1, 64, 1, 96, 64, a, a, None) == 2
+    assert lib.tilemix_quantize_blockwise(a, 128, 128, a, 1, 64, 1, 128, 32, a, a, None) == 2
+    assert lib.tilemix_quantize_blockwise(a, 129, 128, a, 1, 64, 1, 128, 64, a, a, None) == 1
+    assert lib.tilemix_quantize_blockwise(a, 128, 128, None, 1, 64, 1, 128, 64, a, a, None) == 1
+    assert lib.tilemix_build_route_mask(a, a, 1, 64 * 65, 1, 1, a, None) == 3
+    assert lib.tilemix_build_route_mask(a, a, 1, 64 * 65, 1, 0, a, None) == 1
+    assert lib.tilemix_build_route_mask(None, a, 1, 64, 1, 1, a, None) == 1
+    assert lib.tilemix_decode_route_mask(a, a, 1, 64 * 129, 1, 2, a, None) == 3
+    assert "64-bit" in tm.last_error()

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: bit-exact for the quantiser (int8 values and fp32 scales), the route
+words and their decode, the INT32 score tiles and the tile-visit counts;
+outputs (fp32 output option) within max-abs 2e-3 and relative Frobenius 1e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from workloads import config, make_workload
+from tests.oracle_inputs import oracle_inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-3
+REL_FRO = 1e-3
+
+
+@pytest.fixture(scope="module")
+def gp():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_path
+    return gpu_path
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ quantiser
+QUANT_CASES = [
+    ("tiny_d64_blk64", dict(lengths=[512], hq=1, hk=1, d=64), 64),
+    ("varlen_d128_blk64", dict(lengths=[1, 63, 64, 65, 200, 129], hq=3, hk=1, d=128), 64),
+    ("varlen_d128_blk128", dict(lengths=[1, 127, 128, 129, 300], hq=2, hk=2, d=128), 128),
+    ("varlen_d64_blk128", dict(lengths=[5, 190, 256], hq=5, hk=1, d=64), 128),
+]
+
+
+@pytest.mark.parametrize("name,shape,blk", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
+def test_quantize_bitexact(gp, name, shape, blk):
+    import torch
+    _announce(f"quantize {name}")
+    w = make_workload(300, lengths=shape["lengths"], num_q_heads=shape["hq"], num_kv_heads=shape["hk"],
+                      head_dim=shape["d"], g=1, outliers=True)
+    w.q[: min(64, w.q.shape[0]), 0] = 0          # an all-zero block
+    t = gp.upload(w)
+    qq, qs = gp.tm.tilemix_quantize_blockwise(t["q"], t["cu"], w.max_seqlen, blk)
+    torch.cuda.synchronize()
+    rq, rs = orc.quantize_blockwise(w.q, w.cu_seqlens, w.max_seqlen, blk)
+    assert np.array_equal(qq.cpu().numpy(), rq)
+    assert np.array_equal(qs.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantize_strided_input(gp):
+    """Q as a view into a packed QKV buffer (token stride > heads*d)."""
+    import torch
+    _announce("quantize strided")
+    w = make_workload(301, lengths=[70, 130], num_q_heads=4, num_kv_heads=2, head_dim=128, g=1, outliers=True)
+    N = w.q.shape[0]
+    qkv = torch.zeros((N, 8, 128), dtype=torch.float16, device="cuda:0")
+    qkv[:, :4] = torch.from_numpy(w.q).cuda()
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    qq, qs = gp.tm.tilemix_quantize_blockwise(qkv[:, :4], cu, w.max_seqlen, 64)
+    torch.cuda.synchronize()
+    rq, rs = orc.quantize_blockwise(w.q, w.cu_seqlens, w.max_seqlen, 64)
+    assert np.array_equal(qq.cpu().numpy(), rq)
+    assert np.array_equal(qs.cpu().numpy(), rs)
+
+
+# ------------------------------------------------------------------ route words
+@pytest.mark.parametrize("g", [1, 2, 3, 16])
+def test_route_mask_bitexact(gp, g):
+    import torch
+    _announce(f"route mask g={g}")
+    lengths = [1, 64, 65, 64 * 40 + 7]
+    w = make_workload(310 + g, lengths=lengths, num_q_heads=2, num_kv_heads=2, head_dim=64, g=1)
+    rng = np.random.default_rng(g)
+    T = w.T
+    tr = rng.integers(0, 3, size=(2, len(lengths), T, T)).astype(np.uint8)
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    words = gp.tm.tilemix_build_route_mask(torch.from_numpy(tr).cuda(), cu, w.max_seqlen, g)
+    dec = gp.tm.tilemix_decode_route_mask(words, cu, w.max_seqlen, g)
+    torch.cuda.synchronize()
+    ref = orc.build_route_mask(tr, w.cu_seqlens, w.max_seqlen, g)
+    assert np.array_equal(gp.words_u64(words), ref)
+    assert np.array_equal(dec.cpu().numpy(), orc.decode_route_mask(ref, w.cu_seqlens, w.max_seqlen, g))
+
+
+def test_route_mask_too_many_groups(gp):
+    import torch
+    from mixed_precision_amd.tilemix import TilemixError
+    cu = torch.tensor([0, 64 * 65], dtype=torch.int32, device="cuda:0")
+    tr = torch.zeros((1, 1, 65, 65), dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(TilemixError) as e:
+        gp.tm.tilemix_build_route_mask(tr, cu, 64 * 65, 1)
+    assert e.value.status == 3
+
+
+# ------------------------------------------------------------------ attention, small, compared in full
+SMALL = [
+    # name, lengths, Hq, Hk, d, g, route, p, kv_int8, blk_q, outliers
+    ("tiny_L512_d64", [512], 1, 1, 64, 1, "bernoulli", 0.5, False, 64, False),
+    ("len1", [1], 2, 1, 64, 1, "bernoulli", 0.5, False, 64, False),
+    ("ragged_gqa3_d128", [1, 65, 200, 130], 3, 1, 128, 1, "bernoulli", 0.75, False, 64, True),
+    ("gqa4_varlen_g2", [300, 64, 127], 8, 2, 128, 2, "bernoulli", 0.5, False, 64, True),
+    ("gqa2_d64", [257, 129], 4, 2, 64, 1, "bernoulli", 0.5, False, 128, True),
+    ("gqa7_two_chunks", [190], 7, 1, 128, 1, "bernoulli", 0.5, False, 64, False),
+    ("all_fp16", [333], 3, 1, 128, 1, "zeros", 0.0, False, 64, True),
+    ("all_int8", [333], 3, 1, 128, 1, "ones", 1.0, False, 64, True),
+    ("blkq128", [400, 77], 6, 2, 128, 1, "bernoulli", 0.5, False, 128, True),
+    ("kv_int8_gqa7_g4", [520, 100], 7, 1, 128, 4, "bernoulli", 0.5, True, 64, False),
+    ("kv_int8_d64", [300], 2, 1, 64, 1, "bernoulli", 0.5, True, 64, False),
+    ("band_sink_g2", [700, 450], 4, 1, 128, 2, "band_sink", 0.0, False, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_attn_small_full(gp, case):
+    import torch
+    name, lengths, hq, hk, d, g, route, p, kv8, blk_q, outl = case
+    _announce(f"attn small {name}")
+    w = make_workload(400 + SMALL.index(case), lengths=lengths, num_q_heads=hq, num_kv_heads=hk, head_dim=d, g=g,
+                      route=route, p=p, kv_int8=kv8, blk_q=blk_q, outliers=outl)
+    t = gp.prepare(w)
+    out = gp.attn(w, t, out_fp32=True)
+    out16 = gp.attn(w, t, out_fp32=False)
+    torch.cuda.synchronize()
+    ref = orc.attn_prefill(oracle_inputs(w))
+    ma, rf = gp.errors(out.cpu().numpy(), ref)
+    print(f"  max_abs={ma:.3e} rel_fro={rf:.3e}")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+    # fp16 output: within half an fp16 ulp of the reference plus the same budget
+    o16 = out16.cpu().numpy().astype(np.float64)
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(o16 - ref) <= 0.5 * ulp + MAX_ABS)
+    # the first query of each sequence sees only its own key: O = V_eff[0]
+    inp = oracle_inputs(w)
+    for b, (s0, L) in enumerate(orc.seq_spans(w.cu_seqlens)):
+        for h in range(hq):
+            v0 = inp._kv(b, inp.kv_head(h))[1][0]
+            assert np.max(np.abs(out.cpu().numpy()[s0, h] - v0)) <= 1e-3 * max(1.0, np.max(np.abs(v0)))
+
+
+@pytest.mark.parametrize("case", ["tiny", "gqa3_varlen", "kv_int8"])
+def test_attn_debug_bitexact(gp, case):
+    """INT32 score tiles bit-exact; every legal tile visited once, nothing else;
+    the decoded route per visited tile equals the oracle's."""
+    import torch
+    _announce(f"attn debug {case}")
+    if case == "tiny":
+        w = config(1)
+        seq, head = 0, 0
+    elif case == "gqa3_varlen":
+        w = make_workload(450, lengths=[130, 300, 64], num_q_heads=6, num_kv_heads=2, head_dim=128, g=2,
+                          p=0.6, outliers=True)
+        seq, head = 1, 4
+    else:
+        w = make_workload(451, lengths=[260, 90], num_q_heads=7, num_kv_heads=1, head_dim=128, g=1, p=0.5,
+                          kv_int8=True)
+        seq, head = 0, 5
+    t = gp.prepare(w)
+    out, s32, visits, used = gp.attn_debug(w, t, seq=seq, q_head=head)
+    torch.cuda.synchronize()
+    inp = oracle_inputs(w)
+    ref_s32 = orc.s32_tiles(inp, seq, head, 0, w.T)
+    assert np.array_equal(s32.cpu().numpy(), ref_s32)
+    vis = orc.visit_matrix(w.cu_seqlens, w.max_seqlen, w.num_q_heads)
+    assert np.array_equal(visits.cpu().numpy().astype(np.uint32), vis)
+    assert np.array_equal(used.cpu().numpy(), orc.route_used(inp))
+    ma, rf = gp.errors(out.cpu().numpy(), orc.attn_prefill(inp))
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+def test_attn_g1_equals_g4_when_groups_constant(gp):
+    """Same per-tile routes packed at g = 1 and g = 4 give identical outputs."""
+    import torch
+    _announce("attn g1 vs g4")
+    w4 = make_workload(460, lengths=[64 * 12 + 5], num_q_heads=3, num_kv_heads=1, head_dim=128, g=4, p=0.5,
+                       outliers=True)
+    t = gp.prepare(w4)
+    o4 = gp.attn(w4, t).clone()
+    w1 = make_workload(460, lengths=[64 * 12 + 5], num_q_heads=3, num_kv_heads=1, head_dim=128, g=4, p=0.5,
+                       outliers=True)
+    w1.g = 1
+    t1 = gp.prepare(w1, t={k: v for k, v in t.items() if k in ("q", "k", "v", "cu", "tile_route")})
+    o1 = gp.attn(w1, t1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o4)
+
+
+# ------------------------------------------------------------------ standard workloads
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_standard_config_scaled_full(gp, cfg):
+    """Each standard workload's structure at 1/8 of its lengths (1/16 for the
+    long one), compared in full."""
+    import torch
+    _announce(f"config {cfg} scaled")
+    w = config(cfg, scale_down=1 if cfg == 1 else (16 if cfg == 5 else 8))
+    t = gp.prepare(w)
+    out = gp.attn(w, t)
+    torch.cuda.synchronize()
+    ref = orc.attn_prefill(oracle_inputs(w))
+    ma, rf = gp.errors(out.cpu().numpy(), ref)
+    print(f"  {w.name}: max_abs={ma:.3e} rel_fro={rf:.3e}")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+def _samples(w, rng, n):
+    spans = orc.seq_spans(w.cu_seqlens)
+    lens = [L for _, L in spans]
+    out = set()
+    G = w.num_q_heads // w.num_kv_heads
+    b_long, b_short = int(np.argmax(lens)), int(np.argmin(lens))
+    for b in {b_long, b_short, 0}:
+        Tb = orc.num_tiles(lens[b])
+        for m in {0, 1, Tb - 1, Tb - 2}:
+            if 0 <= m < Tb:
+                for hk in range(w.num_kv_heads):
+                    out.add((b, hk * G + int(rng.integers(G)), m))
+        for j in range(0, min(64, (Tb + w.g - 1) // w.g)):   # group boundaries
+            for m in (j * w.g, j * w.g + w.g - 1):
+                if m < Tb and len(out) < n // 2:
+                    out.add((b, int(rng.integers(w.num_q_heads)), m))
+    while len(out) < n:
+        b = int(rng.integers(len(lens)))
+        out.add((b, int(rng.integers(w.num_q_heads)), int(rng.integers(orc.num_tiles(lens[b])))))
+    return sorted(out)
+
+
+@pytest.mark.parametrize("cfg,nsamp", [(2, 96), (3, 48), (4, 24), (5, 12)])
+def test_standard_config_full_size_sampled(gp, cfg, nsamp):
+    """Full-size workloads in the launch configuration the bench times, checked
+    on sampled query-tile rows (the oracle evaluates each one by one), plus
+    the full int8 operands and route words bit-exact."""
+    import torch
+    _announce(f"config {cfg} full size sampled ({nsamp} rows)")
+    w = config(cfg)
+    t = gp.prepare(w)
+    out = gp.attn(w, t)
+    torch.cuda.synchronize()
+    inp = oracle_inputs(w)
+    assert np.array_equal(gp.words_u64(t["words"]), inp.words)
+    assert np.array_equal(t["q_q"].cpu().numpy(), inp.q_q)
+    assert np.array_equal(t["q_s"].cpu().numpy(), inp.q_scale)
+    rng = np.random.default_rng(cfg)
+    got_all = out.cpu().numpy()
+    errs, num, den = [], 0.0, 0.0
+    for (b, hq, m) in _samples(w, rng, nsamp):
+        s0, L = inp.spans[b]
+        i0, i1 = m * 64, min(m * 64 + 64, L)
+        ref = orc.attn_tile_row(inp, b, hq, m)
+        got = got_all[s0 + i0:s0 + i1, hq].astype(np.float64)
+        errs.append(np.max(np.abs(got - ref)))
+        num += float(np.sum((got - ref) ** 2))
+        den += float(np.sum(ref ** 2))
+    ma, rf = max(errs), (num / den) ** 0.5
+    print(f"  {w.name}: max_abs={ma:.3e} rel_fro={rf:.3e} over {len(errs)} tile rows")
+    assert ma <= MAX_ABS and rf <= REL_FRO
