@@ -90,60 +90,59 @@ struct Attn {
   // r / NB.  The 16 consecutive rows one MFMA operand read touches then fall in
   // 16 different 16-byte bank groups, every operand address is a per-lane base
   // plus an immediate, and one lds-load instruction fills one whole block.
-  static constexpr int BLK = 1040;
-  template <int RB>
+  //
+  // K blocks are padded to 1040 B: a K operand read (16 rows x 16 B per lane
+  // group) then covers all 64 banks once.  V blocks are padded to 1056 B: a
+  // ds_read_b64_tr_b16 has each 16-lane group read 4 consecutive keys x 32 B,
+  // and the 32-byte skew puts the 8 keys of 32 lanes on 256 distinct bytes.
+  template <int RB, int BLK>
   struct Lay {
     static constexpr int NB = 64 / (1024 / RB);
+    static constexpr int BLOCK = BLK;
     static TM_DEV int row(int r) { return (r % NB) * BLK + (r / NB) * RB; }
     // row 16*k + c16 (c16 < 16): per-lane part and compile-time part
     static TM_DEV int lane(int c16) { return (c16 % NB) * BLK + (c16 / NB) * RB; }
     static constexpr int step16 = (16 / NB) * RB;
+    static constexpr int BYTES = NB * BLK;
   };
-  using L16 = Lay<RB16>;
-  using L8 = Lay<RB8>;
-  static constexpr int TBYTES = L16::NB * BLK;             // one fp16 tile (int8 uses half)
-  static constexpr int LDS_BYTES = 4 * TBYTES;             // K and V, double-buffered
+  using L16 = Lay<RB16, 1040>;
+  using L8 = Lay<RB8, 1040>;
+  using LV = Lay<RB16, 1056>;
+  static constexpr int KBYTES = L16::BYTES;                // one K stage (int8 K uses half)
+  static constexpr int VBYTES = LV::BYTES;                 // one V stage
+  static constexpr int LDS_BYTES = 2 * (KBYTES + VBYTES);  // K and V, double-buffered
   static constexpr int NI16 = L16::NB / 4;                 // lds-load instructions per wave, fp16 tile
   static constexpr int NI8 = L8::NB / 4;                   // ... int8 tile
 
   static TM_DEV int k16_off(int R, int C) { return L16::row(R) + C * 16; }
   static TM_DEV int k8_off(int R, int C) { return L8::row(R) + C * 16; }
-  static TM_DEV int v_off(int key, int d) { return L16::row(key) + d * 2; }
+  static TM_DEV int v_off(int key, int d) { return LV::row(key) + d * 2; }
 
   // Per-lane global byte offsets (relative to the tile's first row) of the
-  // lds-loads; instruction i of wave w fills block w*NI + i.
+  // lds-loads.  Instruction i of wave w fills block w*NI + i, whose lanes
+  // hold rows w*NI + i + NB*s (slot s = lane*16 / RB): offset = base + i*stride.
   struct Dma {
-    uint32_t k16[NI16], v[NI16], k8[NI8];
+    uint32_t b16, b8;
   };
-  static TM_DEV void dma_offsets(Dma& o, int wave, int lane, uint32_t k16_stride, uint32_t k8_stride,
-                                 uint32_t v_stride) {
-#pragma unroll
-    for (int i = 0; i < NI16; ++i) {
-      const int q = wave * NI16 + i;
-      const int R = q + L16::NB * ((lane * 16) / RB16), p = ((lane * 16) % RB16) / 16;
-      o.k16[i] = R * k16_stride + p * 16;
-      o.v[i] = R * v_stride + p * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < NI8; ++i) {
-      const int q = wave * NI8 + i;
-      const int R = q + L8::NB * ((lane * 16) / RB8), p = ((lane * 16) % RB8) / 16;
-      o.k8[i] = R * k8_stride + p * 16;
-    }
+  static TM_DEV void dma_offsets(Dma& o, int wave, int lane, uint32_t k16_stride, uint32_t k8_stride) {
+    o.b16 = (uint32_t)(wave * NI16 + L16::NB * ((lane * 16) / RB16)) * k16_stride + ((lane * 16) % RB16);
+    o.b8 = (uint32_t)(wave * NI8 + L8::NB * ((lane * 16) / RB8)) * k8_stride + ((lane * 16) % RB8);
   }
 
-  // --- FP16 KV: issue the lds-loads of tile n (K in its route's form, and V)
-  static TM_DEV void dma_tile(int route, int wave, const Dma& o, __amdgpu_buffer_rsrc_t rk16,
-                              __amdgpu_buffer_rsrc_t rk8, __amdgpu_buffer_rsrc_t rv, char* kl, char* vl) {
+  // --- FP16 KV: issue the lds-loads of tile n (K in its route's form, and V).
+  // K and V rows share one stride.
+  static TM_DEV void dma_tile(int route, int wave, const Dma& o, uint32_t s16, uint32_t s8,
+                              __amdgpu_buffer_rsrc_t rk16, __amdgpu_buffer_rsrc_t rk8, __amdgpu_buffer_rsrc_t rv,
+                              char* kl, char* vl) {
     if (route == 0) {
 #pragma unroll
-      for (int i = 0; i < NI16; ++i) bload16_lds(rk16, o.k16[i], kl + (wave * NI16 + i) * BLK);
+      for (int i = 0; i < NI16; ++i) bload16_lds(rk16, o.b16 + i * s16, kl + (wave * NI16 + i) * L16::BLOCK);
     } else {
 #pragma unroll
-      for (int i = 0; i < NI8; ++i) bload16_lds(rk8, o.k8[i], kl + (wave * NI8 + i) * BLK);
+      for (int i = 0; i < NI8; ++i) bload16_lds(rk8, o.b8 + i * s8, kl + (wave * NI8 + i) * L8::BLOCK);
     }
 #pragma unroll
-    for (int i = 0; i < NI16; ++i) bload16_lds(rv, o.v[i], vl + (wave * NI16 + i) * BLK);
+    for (int i = 0; i < NI16; ++i) bload16_lds(rv, o.b16 + i * s16, vl + (wave * NI16 + i) * LV::BLOCK);
   }
 
   // --- INT8 KV cache: register staging (16 int8 of one row per thread and load)
@@ -231,64 +230,78 @@ struct Attn {
       for (int kk = 0; kk < 2; ++kk) S[j][kk] = __builtin_bit_cast(i32x4, __builtin_convertvector(S[j][kk], f32x4));
   }
 
-  // --- diagonal tile: key offset must not exceed query offset
-  static TM_DEV void mask_diag(i32x4 (&S)[QB][2], int h, const int (&qrow)[QB], int gq) {
+  // --- diagonal tile: a key may not come after the query (key0 = first key
+  // of this lane's rows in the half, qpos[j] = query position)
+  static TM_DEV void mask_diag(i32x4 (&S)[QB][2], int key0, const int (&qpos)[QB]) {
 #pragma unroll
     for (int j = 0; j < QB; ++j)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (32 * h + 16 * kk + gq * 4 + i > qrow[j]) S[j][kk][i] = __builtin_bit_cast(int32_t, -INFINITY);
+          if (key0 + 16 * kk + i > qpos[j]) S[j][kk][i] = __builtin_bit_cast(int32_t, -INFINITY);
   }
 
   // --- shared online-softmax update for half h from raw scores (float bits).
-  // Returns true in lanes whose reference max moved (alpha < 1).
-  static TM_DEV bool softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float vsc, float (&mref)[QB],
-                             float (&lrow)[QB], float (&alpha)[QB], f16x8 (&P)[QB]) {
-    bool moved = false;
+  // Each lane first compares its own keys' max with its reference max; only
+  // when some lane of the wave exceeds it by more than kSlack does the wave
+  // take the reduction over the query's 4 lanes, move the reference and
+  // rescale l and the accumulator (the same decision as reducing first, since
+  // the reduced max exceeds the bound exactly when some lane's max does).
+  static TM_DEV void softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float vsc, float (&mref)[QB],
+                             float (&lrow)[QB], f32x4 (&O)[QB][NDB], f16x8 (&P)[QB]) {
+    float lm[QB];
+    bool up = false;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       // Whole-vector bit casts: clang mis-lowers __builtin_bit_cast applied to
       // a single element of an ext_vector (it reads element 0).
-      float x[2][4];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const f32x4 xv = __builtin_bit_cast(f32x4, S[j][kk]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[kk][i] = xv[i];
-      }
-      float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float tmax = mx * cj[j];
-      const float mnew = (tmax > mref[j] + kSlack) ? tmax : mref[j];
-      alpha[j] = __builtin_amdgcn_exp2f(mref[j] - mnew);
-      moved |= (mnew != mref[j]);
-      mref[j] = mnew;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kk][i], cj[j], -mnew));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kk][i + 1], cj[j], -mnew));
-          f16x2 hv;
-          if (KVI8) {
-            hv = f16x2{(f16)(p0 * vsc), (f16)(p1 * vsc)};
-            lsum += p0 + p1;
-          } else {
-            hv = f16x2{(f16)p0, (f16)p1};
-            lsum = __builtin_amdgcn_fdot2(hv, f16x2{(f16)1.0f, (f16)1.0f}, lsum, false);
-          }
-          P[j][kk * 4 + i] = hv[0];
-          P[j][kk * 4 + i + 1] = hv[1];
-        }
-      }
-      lrow[j] = lrow[j] * alpha[j] + lsum;
+      const f32x4 a = __builtin_bit_cast(f32x4, S[j][0]);
+      const f32x4 b = __builtin_bit_cast(f32x4, S[j][1]);
+      lm[j] = __builtin_elementwise_maximum(
+          __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[0], a[1]), __builtin_elementwise_maximum(a[2], a[3])),
+          __builtin_elementwise_maximum(__builtin_elementwise_maximum(b[0], b[1]), __builtin_elementwise_maximum(b[2], b[3])));
+      up |= lm[j] * cj[j] > mref[j] + kSlack;
     }
-    return moved;
+    if (__any(up)) {
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        float mx = lm[j];
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16));
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+        const float tmax = mx * cj[j];
+        const float mnew = (tmax > mref[j] + kSlack) ? tmax : mref[j];
+        const float alpha = (mnew == mref[j]) ? 1.0f : __builtin_amdgcn_exp2f(mref[j] - mnew);
+        mref[j] = mnew;
+        lrow[j] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) O[j][db] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const f32x4 a = __builtin_bit_cast(f32x4, S[j][0]);
+      const f32x4 b = __builtin_bit_cast(f32x4, S[j][1]);
+      const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      float lsum = 0.0f;
+      u32x4 pk;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t], cj[j], -mref[j]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t + 1], cj[j], -mref[j]));
+        f16x2 hv;
+        if (KVI8) {
+          hv = f16x2{(f16)(p0 * vsc), (f16)(p1 * vsc)};
+          lsum += p0 + p1;
+        } else {
+          hv = f16x2{(f16)p0, (f16)p1};
+          lsum = __builtin_amdgcn_fdot2(hv, f16x2{(f16)1.0f, (f16)1.0f}, lsum, false);
+        }
+        pk[t] = __builtin_bit_cast(uint32_t, hv);
+      }
+      P[j] = __builtin_bit_cast(f16x8, pk);
+      lrow[j] += lsum;
+    }
   }
 
   // --- O^T += V^T P^T for half h.  Lane (c, gq) needs, for channel db*16+c,
@@ -297,11 +310,11 @@ struct Attn {
   static TM_DEV void pv(const char* vl, int h, const f16x8 (&P)[QB], f32x4 (&O)[QB][NDB], int lane) {
     const int gq = lane >> 4, jl = lane & 15;
     // key 32h + 16e + (4gq + jl/4), channels db*16 + 4*(jl%4) .. +3
-    const char* base = vl + L16::lane(4 * gq + (jl >> 2)) + 8 * (jl & 3);
+    const char* base = vl + LV::lane(4 * gq + (jl >> 2)) + 8 * (jl & 3);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const f16x4 lo = read_tr16(base + (2 * h) * L16::step16 + db * 32);
-      const f16x4 hi = read_tr16(base + (2 * h + 1) * L16::step16 + db * 32);
+      const f16x4 lo = read_tr16(base + (2 * h) * LV::step16 + db * 32);
+      const f16x4 hi = read_tr16(base + (2 * h + 1) * LV::step16 + db * 32);
       const f16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
       for (int j = 0; j < QB; ++j) O[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, P[j], O[j][db], 0, 0, 0);
@@ -315,8 +328,8 @@ void attn_prefill_kernel(const AttnArgs a) {
   using A = Attn<D, QB, KVI8>;
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
   __shared__ __attribute__((aligned(1024))) char smem[A::LDS_BYTES];
-  auto kbuf = [&](int i) -> char* { return smem + i * A::TBYTES; };                   // i in 0..1
-  auto vbuf = [&](int i) -> char* { return smem + (2 + i) * A::TBYTES; };             // i in 0..1
+  auto kbuf = [&](int i) -> char* { return smem + i * A::KBYTES; };                   // i in 0..1
+  auto vbuf = [&](int i) -> char* { return smem + 2 * A::KBYTES + i * A::VBYTES; };   // i in 0..1
 
   const WorkItem item = a.items[blockIdx.x];
   const int b = uniform(item.b);
@@ -383,22 +396,23 @@ void attn_prefill_kernel(const AttnArgs a) {
     return make_rsrc(base + (int64_t)n * kTile * stride, (uint32_t)rows * stride);
   };
   typename A::Dma dma;
-  if (!KVI8) A::dma_offsets(dma, wave, lane, kv_stride, k8_stride, kv_stride);
+  if (!KVI8) A::dma_offsets(dma, wave, lane, kv_stride, k8_stride);
 
   const uint64_t word = uniform64(a.words[((int64_t)hk * a.batch + b) * a.T + m]);
   const int g = a.g;
   const float* kscale_row = a.k_scale + ((int64_t)hk * a.batch + b) * a.T;
   const float* vscale_row = KVI8 ? a.v_scale + ((int64_t)hk * a.batch + b) * a.T : nullptr;
-  auto route_of = [&](int n) -> int {
-    const int grp = n / g;
-    return grp < 64 ? (int)((word >> grp) & 1ull) : 0;
-  };
-  auto fetch = [&](int n, typename A::Stage& st) {     // start the loads of tile n
+  // Route of tile n = bit floor(n/g) of the word, tracked incrementally:
+  // bit 0 of wsh is the current tile's group, `left` counts the tiles the
+  // group still covers (groups past bit 63 shift in zeros = FP16).
+  uint64_t wsh = word;
+  int left = g;
+  auto fetch = [&](int n, int route, typename A::Stage& st) {     // start the loads of tile n
     if (KVI8) {
       A::stage_load(st, tid, tile_rsrc(kbase, kv_stride, n), tile_rsrc(vbase, kv_stride, n), kv_stride);
     } else {
-      A::dma_tile(route_of(n), wave, dma, tile_rsrc(kbase, kv_stride, n), tile_rsrc(k8base, k8_stride, n),
-                  tile_rsrc(vbase, kv_stride, n), kbuf(n & 1), vbuf(n & 1));
+      A::dma_tile(route, wave, dma, kv_stride, k8_stride, tile_rsrc(kbase, kv_stride, n),
+                  tile_rsrc(k8base, k8_stride, n), tile_rsrc(vbase, kv_stride, n), kbuf(n & 1), vbuf(n & 1));
     }
   };
 
@@ -416,8 +430,8 @@ void attn_prefill_kernel(const AttnArgs a) {
   // ---- prologue: tile 0 into stage 0
   {
     typename A::Stage st;
-    fetch(0, st);
-    if (KVI8) A::stage_store(st, route_of(0), tid, kbuf(0), vbuf(0));
+    fetch(0, (int)(wsh & 1), st);
+    if (KVI8) A::stage_store(st, (int)(wsh & 1), tid, kbuf(0), vbuf(0));
   }
   wait_vmem();
   __syncthreads();
@@ -427,16 +441,21 @@ void attn_prefill_kernel(const AttnArgs a) {
   // One loop body serves every tile; only the QK^T path and the diagonal mask
   // branch (uniformly) inside it.
   for (int n = 0; n <= m; ++n) {
-    const int rc = route_of(n);
+    const int rc = (int)(wsh & 1);
+    const int rnext = (left == 1) ? (int)((wsh >> 1) & 1) : rc;
     const bool last = (n == m);
     const char* kl = kbuf(n & 1);
     const char* vl = vbuf(n & 1);
     typename A::Stage st;
-    if (!last) fetch(n + 1, st);
+    if (!last) fetch(n + 1, rnext, st);
     const float ksc = kscale_row[n];
     float cj[QB];
 #pragma unroll
-    for (int j = 0; j < QB; ++j) cj[j] = rc ? sq[j] * ksc * a.sm_log2 : (KVI8 ? ksc * a.sm_log2 : a.sm_log2);
+    for (int j = 0; j < QB; ++j) {
+      // kept > 0 so a (caller-supplied) zero scale cannot turn a masked -inf into NaN
+      cj[j] = rc ? sq[j] * ksc * a.sm_log2 : (KVI8 ? ksc * a.sm_log2 : a.sm_log2);
+      cj[j] = __builtin_elementwise_maximum(cj[j], 1.17549435e-38f);
+    }
     const float vsc = KVI8 ? vscale_row[n] : 1.0f;
     if (DBG) {
 #pragma unroll
@@ -470,26 +489,23 @@ void attn_prefill_kernel(const AttnArgs a) {
         A::int_to_float_bits(S);
       }
       if (last) {
-        int qrow[QB];
+        int qpos[QB];
 #pragma unroll
-        for (int j = 0; j < QB; ++j) qrow[j] = qb_row(j);
-        A::mask_diag(S, h, qrow, gq);
+        for (int j = 0; j < QB; ++j) qpos[j] = m * kTile + qb_row(j);
+        A::mask_diag(S, n * kTile + 32 * h + 4 * gq, qpos);
       }
       f16x8 P[QB];
-      float alpha[QB];
-      const bool moved = A::softmax(S, cj, vsc, mref, lrow, alpha, P);
-      if (__any(moved)) {
-#pragma unroll
-        for (int j = 0; j < QB; ++j)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) O[j][db] *= alpha[j];
-      }
+      A::softmax(S, cj, vsc, mref, lrow, O, P);
       A::pv(vl, h, P, O, lane);
     }
     if (!last) {
-      if (KVI8) A::stage_store(st, route_of(n + 1), tid, kbuf((n + 1) & 1), vbuf((n + 1) & 1));
+      if (KVI8) A::stage_store(st, rnext, tid, kbuf((n + 1) & 1), vbuf((n + 1) & 1));
       wait_vmem();
       __syncthreads();
+    }
+    if (--left == 0) {
+      left = g;
+      wsh >>= 1;
     }
   }
 

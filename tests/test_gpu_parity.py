@@ -177,6 +177,29 @@ def test_attn_debug_bitexact(gp, case):
     assert ma <= MAX_ABS and rf <= REL_FRO
 
 
+def test_attn_zero_scale_blocks(gp):
+    """A caller may pass scale 0 for an all-zero INT8 block (the library's own
+    quantiser writes 1.0 there).  The INT32 scores of such a block are 0 either
+    way, so the output must equal the oracle's, masked keys included."""
+    import torch
+    _announce("attn zero-scale blocks")
+    w = make_workload(470, lengths=[200, 150], num_q_heads=3, num_kv_heads=1, head_dim=128, g=1, route="ones",
+                      p=1.0, outliers=True)
+    s1 = int(w.cu_seqlens[1])
+    w.q[64:128, 1, :] = 0            # seq 0, query tile 1 of head 1 (diagonal tile is INT8)
+    w.k[s1 + 64:s1 + 128, 0, :] = 0  # seq 1, key tile 1
+    t = gp.prepare(w)
+    t["q_s"][1, 0, 1] = 0.0
+    t["k_s"][0, 1, 1] = 0.0
+    out = gp.attn(w, t)
+    torch.cuda.synchronize()
+    ref = orc.attn_prefill(oracle_inputs(w))
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    ma, rf = gp.errors(got, ref)
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
 def test_attn_g1_equals_g4_when_groups_constant(gp):
     """Same per-tile routes packed at g = 1 and g = 4 give identical outputs."""
     import torch
