@@ -72,9 +72,10 @@ struct SchedArgs {
   int32_t batch, T, Hk, nch;
   int64_t nslots, segmax;
   WorkItem* items;
-  int32_t* seg;      // int32 [segmax][5]: slot_begin, count, item_begin, b, hk
-  int32_t* segidx;   // int32 [kNumXcd + 1]: per-XCD offsets into seg
-  int32_t* order;    // int32 [batch]: sequences by decreasing tile count
+  int32_t* seg;      // int32 [segmax][6]: xcd, slot_begin, count, item_begin, b, hk
+  int32_t* segidx;   // int32 [1 + kNumXcd]: segment count, then slots used per XCD
+  int32_t* order;    // int32 [2 * batch]: sequences by decreasing tile count, then tile counts
+                     // (used only when batch exceeds what the plan kernel keeps in LDS)
 };
 
 WorkspaceLayout workspace_layout(int32_t batch, int32_t T, int32_t Hk, int32_t nch);

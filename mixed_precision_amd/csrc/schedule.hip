@@ -19,128 +19,144 @@
 //     decreasing m (longest causal rows first), so the short rows fill the tail.
 // Slot i of the grid then takes entry i / 8 of XCD (i % 8)'s list.
 //
-// plan: one workgroup (the greedy placement is sequential, O(groups * 8)).
-// emit: one thread per slot, binary search of its XCD's segment table.
+// plan: one workgroup.  Tile counts and the rank sort live in LDS (global
+//   scratch past kPlanLdsBatch sequences); the greedy placement runs in wave 0
+//   as wave-uniform scalar code and writes each segment to the segment table
+//   without reading it back, then the segment count and per-XCD fill levels.
+// emit: one workgroup per segment writes that segment's items; 8 more
+//   workgroups mark each XCD's unused slots empty (b = -1).
 #include "device_common.hpp"
 #include "internal.hpp"
 
 namespace tilemix {
 
 namespace {
-constexpr int kSegFields = 6;   // xcd, slot_begin, count, item_begin, b, hk
-
-__device__ __forceinline__ int tiles_of(const int32_t* cu, int b) {
-  return (cu[b + 1] - cu[b] + kTile - 1) / kTile;
-}
+constexpr int kSegFields = 6;           // xcd, slot_begin, count, item_begin, b, hk
+constexpr int kPlanLdsBatch = 4096;     // sequences whose tile counts / order fit in LDS
 }  // namespace
 
 __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
+  __shared__ int32_t s_tiles[kPlanLdsBatch];
+  __shared__ int32_t s_order[kPlanLdsBatch];
+  const bool in_lds = a.batch <= kPlanLdsBatch;
+  int32_t* tiles = in_lds ? s_tiles : a.order + a.batch;
+  int32_t* order = in_lds ? s_order : a.order;
+
+  for (int b = threadIdx.x; b < a.batch; b += 256) tiles[b] = (a.cu[b + 1] - a.cu[b] + kTile - 1) / kTile;
+  __syncthreads();
   // 1) sequences ordered by decreasing tile count (ties by index): rank sort.
   for (int b = threadIdx.x; b < a.batch; b += 256) {
-    const int tb = tiles_of(a.cu, b);
+    const int tb = tiles[b];
     int rank = 0;
     for (int o = 0; o < a.batch; ++o) {
-      const int to = tiles_of(a.cu, o);
+      const int to = tiles[o];
       rank += (to > tb) || (to == tb && o < b);
     }
-    a.order[rank] = b;
+    order[rank] = b;
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  if (threadIdx.x >= 64) return;
 
-  // 2) greedy placement of (b, hk) groups on XCDs, raw segments in creation order.
+  // 2) greedy placement of (b, hk) groups on XCDs (every value is wave-uniform;
+  //    the per-XCD state is indexed with compile-time indices only).
+  const int lane = threadIdx.x;
   const int64_t cap = a.nslots / kNumXcd;
-  int64_t used[kNumXcd];
-  int64_t load[kNumXcd];
+  int64_t used[kNumXcd], load[kNumXcd];
+#pragma unroll
   for (int x = 0; x < kNumXcd; ++x) used[x] = load[x] = 0;
-  int32_t* raw = a.seg;                                   // [segmax][6]
-  int32_t* sorted = a.seg + a.segmax * kSegFields;        // [segmax][6]
   int64_t nseg = 0;
   for (int r = 0; r < a.batch; ++r) {
-    const int b = a.order[r];
-    const int tb = tiles_of(a.cu, b);
-    if (tb == 0) continue;
+    const int b = uniform(order[r]);
+    const int tb = uniform(tiles[b]);
+    if (tb == 0) break;                           // sorted: the rest are empty too
     const int64_t cnt = (int64_t)tb * a.nch;
     const int64_t cost = (int64_t)a.nch * tb * (tb + 1) / 2;
     for (int hk = 0; hk < a.Hk; ++hk) {
       int64_t remaining = cnt, ib = 0;
       while (remaining > 0 && nseg < a.segmax) {
         int best = -1;
+        int64_t best_load = 0;
+#pragma unroll
         for (int x = 0; x < kNumXcd; ++x)
-          if (cap - used[x] >= remaining && (best < 0 || load[x] < load[best])) best = x;
+          if (cap - used[x] >= remaining && (best < 0 || load[x] < best_load)) {
+            best = x;
+            best_load = load[x];
+          }
         int64_t take = remaining;
-        if (best < 0) {
+        if (best < 0) {                           // split: XCD with the most free slots
           best = 0;
+          int64_t best_free = cap - used[0];
+#pragma unroll
           for (int x = 1; x < kNumXcd; ++x)
-            if (cap - used[x] > cap - used[best]) best = x;
-          take = cap - used[best];
-          if (take <= 0) break;      // cannot happen: slots >= items
+            if (cap - used[x] > best_free) {
+              best = x;
+              best_free = cap - used[x];
+            }
+          take = best_free;
+          if (take <= 0) break;                   // cannot happen: slots >= items
         }
-        int32_t* s = raw + nseg * kSegFields;
-        s[0] = best;
-        s[1] = (int32_t)used[best];
-        s[2] = (int32_t)take;
-        s[3] = (int32_t)ib;
-        s[4] = b;
-        s[5] = hk;
+        int64_t slot_begin = 0;
+#pragma unroll
+        for (int x = 0; x < kNumXcd; ++x) slot_begin = (x == best) ? used[x] : slot_begin;
+        if (lane == 0) {
+          int32_t* sg = a.seg + nseg * kSegFields;
+          sg[0] = best;
+          sg[1] = (int32_t)slot_begin;
+          sg[2] = (int32_t)take;
+          sg[3] = (int32_t)ib;
+          sg[4] = b;
+          sg[5] = hk;
+        }
+        const int64_t add = (take == cnt) ? cost : cost * take / cnt;
+#pragma unroll
+        for (int x = 0; x < kNumXcd; ++x)
+          if (x == best) {
+            used[x] += take;
+            load[x] += add;
+          }
         ++nseg;
-        used[best] += take;
-        load[best] += cost * take / cnt;
         ib += take;
         remaining -= take;
       }
     }
   }
-  // 3) per-XCD segment lists (increasing slot_begin inside each XCD).
-  int64_t k = 0;
-  for (int x = 0; x < kNumXcd; ++x) {
-    a.segidx[x] = (int32_t)k;
-    for (int64_t i = 0; i < nseg; ++i) {
-      const int32_t* s = raw + i * kSegFields;
-      if (s[0] != x) continue;
-      int32_t* d = sorted + k * kSegFields;
-      for (int f = 0; f < kSegFields; ++f) d[f] = s[f];
-      ++k;
-    }
+  if (lane == 0) {
+    a.segidx[0] = (int32_t)nseg;
+#pragma unroll
+    for (int x = 0; x < kNumXcd; ++x) a.segidx[1 + x] = (int32_t)used[x];
   }
-  a.segidx[kNumXcd] = (int32_t)k;
 }
 
 __global__ __launch_bounds__(256) void schedule_emit_kernel(SchedArgs a) {
-  const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (slot >= a.nslots) return;
-  const int x = (int)(slot % kNumXcd);
-  const int64_t pos = slot / kNumXcd;
-  const int32_t* sorted = a.seg + a.segmax * kSegFields;
-  int lo = a.segidx[x], hi = a.segidx[x + 1] - 1;
-  WorkItem it{-1, 0, 0, 0};
-  while (lo <= hi) {
-    const int mid = (lo + hi) >> 1;
-    const int32_t* s = sorted + (int64_t)mid * kSegFields;
-    if (pos < s[1]) {
-      hi = mid - 1;
-    } else if (pos >= (int64_t)s[1] + s[2]) {
-      lo = mid + 1;
-    } else {
-      const int b = s[4];
-      const int tb = tiles_of(a.cu, b);
-      const int64_t t = s[3] + (pos - s[1]);
-      it.b = b;
-      it.hk = s[5];
-      it.m = tb - 1 - (int)(t / a.nch);
-      it.chunk = (int)(t % a.nch);
-      break;
-    }
+  const int64_t w = blockIdx.x;
+  const int64_t cap = a.nslots / kNumXcd;
+  if (w >= a.segmax) {                              // empty tail of XCD x
+    const int x = (int)(w - a.segmax);
+    const int64_t used = uniform(a.segidx[1 + x]);
+    for (int64_t pos = used + threadIdx.x; pos < cap; pos += 256)
+      a.items[pos * kNumXcd + x] = WorkItem{-1, 0, 0, 0};
+    return;
   }
-  a.items[slot] = it;
+  if (w >= uniform(a.segidx[0])) return;
+  const int32_t* sg = a.seg + w * kSegFields;
+  const int x = uniform(sg[0]);
+  const int64_t slot_begin = uniform(sg[1]);
+  const int count = uniform(sg[2]);
+  const int item_begin = uniform(sg[3]);
+  const int b = uniform(sg[4]);
+  const int hk = uniform(sg[5]);
+  const int tb = (uniform(a.cu[b + 1]) - uniform(a.cu[b]) + kTile - 1) / kTile;
+  for (int i = threadIdx.x; i < count; i += 256) {
+    const int t = item_begin + i;                   // item index inside the group: m descending, chunks inner
+    a.items[(slot_begin + i) * kNumXcd + x] = WorkItem{b, hk, tb - 1 - t / a.nch, t % a.nch};
+  }
 }
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(schedule_plan_kernel, dim3(1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned blocks = (unsigned)((a.nslots + 255) / 256);
-  hipLaunchKernelGGL(schedule_emit_kernel, dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(schedule_emit_kernel, dim3((unsigned)(a.segmax + kNumXcd)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -79,6 +79,12 @@ int32_t validate_attn_params(const tilemix_attn_params* p) {
     return fail(TILEMIX_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   int32_t st = check_groups(p->max_seqlen, p->g);
   if (st != TILEMIX_OK) return st;
+  // one workgroup per work item: the grid (256 threads each) must stay below 2^32 threads
+  const int64_t items = (int64_t)p->batch * cdiv(p->max_seqlen, kTile) * p->num_kv_heads *
+                        cdiv(p->num_q_heads / p->num_kv_heads, 3);
+  if (items > (int64_t)1 << 24)
+    return fail(TILEMIX_ERR_UNSUPPORTED, "%lld work items exceed one launch (2^24); split the batch",
+                (long long)items);
   return TILEMIX_OK;
 }
 
@@ -233,11 +239,11 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t T, int32_t Hk, int32_t n
   w.items_off = off;
   off = up(off + (size_t)w.nslots * sizeof(WorkItem));
   w.seg_off = off;
-  off = up(off + (size_t)w.segmax * 2 * 6 * sizeof(int32_t));
+  off = up(off + (size_t)w.segmax * 6 * sizeof(int32_t));
   w.segidx_off = off;
   off = up(off + (kNumXcd + 1) * sizeof(int32_t));
   w.order_off = off;
-  off = up(off + (size_t)batch * sizeof(int32_t));
+  off = up(off + (size_t)batch * 2 * sizeof(int32_t));
   w.total = off;
   return w;
 }
