@@ -28,7 +28,7 @@ CXXFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-rdc", "-Wno-unused-result",
     "-I", INCLUDE, "-I", CSRC,
-]
+] + os.environ.get("TILEMIX_EXTRA_FLAGS", "").split()
 
 
 def hipcc() -> str:

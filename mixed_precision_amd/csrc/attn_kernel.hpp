@@ -43,10 +43,10 @@
 //    (FP16 path) or q_scale*k_scale*sm_scale*log2(e) (INT8 path), so both paths
 //    meet in one running max and p = exp2(raw*c - m) is one FMA plus v_exp_f32.
 //    The reference max only moves when a half-tile's max exceeds it by more
-//    than kSlack, so the accumulator is rescaled on few tiles; acc / l is
-//    unchanged.  Raw scores are held in integer-typed registers (INT8 results
-//    as int32, FP16 results as their float bits) so no float transformation
-//    ever touches an int32 bit pattern.
+//    than kSlack, so the accumulator is rescaled on few tiles (per q-block,
+//    only where it moved); acc / l is unchanged.  Raw scores are held in
+//    integer-typed registers (INT8 results as int32, FP16 results as their
+//    float bits) so no float transformation ever touches an int32 bit pattern.
 //  * With an fp16 V the normaliser l sums the fp16-rounded probabilities that
 //    actually enter P.V (v_dot2_f32_f16), so O is an exact weighted mean of V
 //    rows with slightly perturbed weights and the dominant term's rounding
@@ -55,9 +55,12 @@
 #include "device_common.hpp"
 #include "internal.hpp"
 
+#ifndef TM_SETPRIO
+#define TM_SETPRIO 3
+#endif
+
 namespace tilemix {
 
-constexpr float kSlack = 8.0f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -80,6 +83,11 @@ TM_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) on
 
 template <int D, int QB, bool KVI8>
 struct Attn {
+  // The reference max may lag the true running max by up to kSlack (log2
+  // units), so p <= 2^kSlack.  FP16 V: p itself must stay finite in fp16
+  // (2^15 < 65504).  INT8 V: p * v_scale goes to fp16, so 2^8 keeps it finite
+  // for any |V| below 32,500 (v_scale < 256).
+  static constexpr float kSlack = KVI8 ? 8.0f : 15.0f;
   static constexpr int NDS = D / 32;       // fp16 MFMA k-steps over d
   static constexpr int NDS8 = D / 64;      // int8 MFMA k-steps over d
   static constexpr int NDB = D / 16;       // 16-row blocks of d in O^T
@@ -270,12 +278,14 @@ struct Attn {
         mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16));
         mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
         const float tmax = mx * cj[j];
-        const float mnew = (tmax > mref[j] + kSlack) ? tmax : mref[j];
-        const float alpha = (mnew == mref[j]) ? 1.0f : __builtin_amdgcn_exp2f(mref[j] - mnew);
-        mref[j] = mnew;
+        const bool moved = tmax > mref[j] + kSlack;
+        const float alpha = moved ? __builtin_amdgcn_exp2f(mref[j] - tmax) : 1.0f;
+        mref[j] = moved ? tmax : mref[j];
         lrow[j] *= alpha;
+        if (__any(moved)) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) O[j][db] *= alpha;
+          for (int db = 0; db < NDB; ++db) O[j][db] *= alpha;
+        }
       }
     }
 #pragma unroll
@@ -471,6 +481,7 @@ void attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       i32x4 S[QB][2];
+      if (TM_SETPRIO & 1) __builtin_amdgcn_s_setprio(1);
       if (rc == 0) {
         A::qk16(kl, h, qf, S, c, gq);
       } else {
@@ -494,9 +505,12 @@ void attn_prefill_kernel(const AttnArgs a) {
         for (int j = 0; j < QB; ++j) qpos[j] = m * kTile + qb_row(j);
         A::mask_diag(S, n * kTile + 32 * h + 4 * gq, qpos);
       }
+      if (TM_SETPRIO & 1) __builtin_amdgcn_s_setprio(0);
       f16x8 P[QB];
       A::softmax(S, cj, vsc, mref, lrow, O, P);
+      if (TM_SETPRIO & 2) __builtin_amdgcn_s_setprio(1);
       A::pv(vl, h, P, O, lane);
+      if (TM_SETPRIO & 2) __builtin_amdgcn_s_setprio(0);
     }
     if (!last) {
       if (KVI8) A::stage_store(st, rnext, tid, kbuf((n + 1) & 1), vbuf((n + 1) & 1));

@@ -21,8 +21,9 @@
 //
 // plan: one workgroup.  Tile counts and the rank sort live in LDS (global
 //   scratch past kPlanLdsBatch sequences); the greedy placement runs in wave 0
-//   as wave-uniform scalar code and writes each segment to the segment table
-//   without reading it back, then the segment count and per-XCD fill levels.
+//   as wave-uniform 32-bit scalar code and writes each segment to the segment
+//   table without reading it back, then the segment count and per-XCD fill
+//   levels.
 // emit: one workgroup per segment writes that segment's items; 8 more
 //   workgroups mark each XCD's unused slots empty (b = -1).
 #include "device_common.hpp"
@@ -35,12 +36,12 @@ constexpr int kSegFields = 6;           // xcd, slot_begin, count, item_begin, b
 constexpr int kPlanLdsBatch = 4096;     // sequences whose tile counts / order fit in LDS
 }  // namespace
 
+template <bool kLds>
 __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
-  __shared__ int32_t s_tiles[kPlanLdsBatch];
-  __shared__ int32_t s_order[kPlanLdsBatch];
-  const bool in_lds = a.batch <= kPlanLdsBatch;
-  int32_t* tiles = in_lds ? s_tiles : a.order + a.batch;
-  int32_t* order = in_lds ? s_order : a.order;
+  __shared__ int32_t s_tiles[kLds ? kPlanLdsBatch : 1];
+  __shared__ int32_t s_order[kLds ? kPlanLdsBatch : 1];
+  int32_t* tiles = kLds ? s_tiles : a.order + a.batch;
+  int32_t* order = kLds ? s_order : a.order;
 
   for (int b = threadIdx.x; b < a.batch; b += 256) tiles[b] = (a.cu[b + 1] - a.cu[b] + kTile - 1) / kTile;
   __syncthreads();
@@ -57,49 +58,52 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
   __syncthreads();
   if (threadIdx.x >= 64) return;
 
-  // 2) greedy placement of (b, hk) groups on XCDs (every value is wave-uniform;
-  //    the per-XCD state is indexed with compile-time indices only).
+  // 2) greedy placement of (b, hk) groups on XCDs.  Every value is
+  //    wave-uniform and 32-bit (scalar ALU); the per-XCD state is indexed with
+  //    compile-time indices only.  Costs are shifted right by cost_shift so
+  //    the largest possible XCD load fits in 31 bits.
   const int lane = threadIdx.x;
-  const int64_t cap = a.nslots / kNumXcd;
-  int64_t used[kNumXcd], load[kNumXcd];
+  const uint32_t cap = (uint32_t)(a.nslots / kNumXcd);
+  uint32_t used[kNumXcd], load[kNumXcd];
 #pragma unroll
   for (int x = 0; x < kNumXcd; ++x) used[x] = load[x] = 0;
-  int64_t nseg = 0;
+  uint32_t nseg = 0;
+  const uint32_t segmax = (uint32_t)a.segmax;
   for (int r = 0; r < a.batch; ++r) {
     const int b = uniform(order[r]);
-    const int tb = uniform(tiles[b]);
+    const uint32_t tb = (uint32_t)uniform(tiles[b]);
     if (tb == 0) break;                           // sorted: the rest are empty too
-    const int64_t cnt = (int64_t)tb * a.nch;
-    const int64_t cost = (int64_t)a.nch * tb * (tb + 1) / 2;
+    const uint32_t cnt = tb * (uint32_t)a.nch;
+    const uint32_t cost = (uint32_t)(((uint64_t)a.nch * tb * (tb + 1) / 2) >> a.cost_shift);
     for (int hk = 0; hk < a.Hk; ++hk) {
-      int64_t remaining = cnt, ib = 0;
-      while (remaining > 0 && nseg < a.segmax) {
+      uint32_t remaining = cnt, ib = 0;
+      while (remaining > 0 && nseg < segmax) {
         int best = -1;
-        int64_t best_load = 0;
+        uint32_t best_load = 0;
 #pragma unroll
-        for (int x = 0; x < kNumXcd; ++x)
-          if (cap - used[x] >= remaining && (best < 0 || load[x] < best_load)) {
-            best = x;
-            best_load = load[x];
-          }
-        int64_t take = remaining;
+        for (int x = 0; x < kNumXcd; ++x) {
+          const bool pick = (cap - used[x] >= remaining) && (best < 0 || load[x] < best_load);
+          best = pick ? x : best;
+          best_load = pick ? load[x] : best_load;
+        }
+        uint32_t take = remaining;
         if (best < 0) {                           // split: XCD with the most free slots
           best = 0;
-          int64_t best_free = cap - used[0];
+          uint32_t best_free = cap - used[0];
 #pragma unroll
-          for (int x = 1; x < kNumXcd; ++x)
-            if (cap - used[x] > best_free) {
-              best = x;
-              best_free = cap - used[x];
-            }
+          for (int x = 1; x < kNumXcd; ++x) {
+            const bool pick = cap - used[x] > best_free;
+            best = pick ? x : best;
+            best_free = pick ? cap - used[x] : best_free;
+          }
           take = best_free;
-          if (take <= 0) break;                   // cannot happen: slots >= items
+          if (take == 0) break;                   // cannot happen: slots >= items
         }
-        int64_t slot_begin = 0;
+        uint32_t slot_begin = 0;
 #pragma unroll
         for (int x = 0; x < kNumXcd; ++x) slot_begin = (x == best) ? used[x] : slot_begin;
         if (lane == 0) {
-          int32_t* sg = a.seg + nseg * kSegFields;
+          int32_t* sg = a.seg + (int64_t)nseg * kSegFields;
           sg[0] = best;
           sg[1] = (int32_t)slot_begin;
           sg[2] = (int32_t)take;
@@ -107,13 +111,12 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
           sg[4] = b;
           sg[5] = hk;
         }
-        const int64_t add = (take == cnt) ? cost : cost * take / cnt;
+        const uint32_t add = (take == cnt) ? cost : (uint32_t)((uint64_t)cost * take / cnt);
 #pragma unroll
-        for (int x = 0; x < kNumXcd; ++x)
-          if (x == best) {
-            used[x] += take;
-            load[x] += add;
-          }
+        for (int x = 0; x < kNumXcd; ++x) {
+          used[x] += (x == best) ? take : 0u;
+          load[x] += (x == best) ? add : 0u;
+        }
         ++nseg;
         ib += take;
         remaining -= take;
@@ -153,7 +156,10 @@ __global__ __launch_bounds__(256) void schedule_emit_kernel(SchedArgs a) {
 }
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(schedule_plan_kernel, dim3(1), dim3(256), 0, s, a);
+  if (a.batch <= kPlanLdsBatch)
+    hipLaunchKernelGGL(schedule_plan_kernel<true>, dim3(1), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(schedule_plan_kernel<false>, dim3(1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(schedule_emit_kernel, dim3((unsigned)(a.segmax + kNumXcd)), dim3(256), 0, s, a);

@@ -117,6 +117,9 @@ SMALL = [
     ("kv_int8_gqa7_g4", [520, 100], 7, 1, 128, 4, "bernoulli", 0.5, True, 64, False),
     ("kv_int8_d64", [300], 2, 1, 64, 1, "bernoulli", 0.5, True, 64, False),
     ("band_sink_g2", [700, 450], 4, 1, 128, 2, "band_sink", 0.0, False, 64, True),
+    # near one-hot rows (Q and K outliers x10): the running max keeps moving
+    ("peaky_rescale_gqa3", [777, 300], 6, 2, 128, 1, "bernoulli", 0.5, False, 64, "peaky"),
+    ("peaky_rescale_kv_int8", [500], 7, 1, 128, 2, "bernoulli", 0.5, True, 64, "peaky"),
     # more sequences than the work-list planner keeps in LDS (global-scratch path)
     ("many_seqs_4100", [1 + (i * 37) % 70 for i in range(4100)], 2, 1, 64, 1, "bernoulli", 0.5, False, 64, False),
 ]
@@ -127,8 +130,9 @@ def test_attn_small_full(gp, case):
     import torch
     name, lengths, hq, hk, d, g, route, p, kv8, blk_q, outl = case
     _announce(f"attn small {name}")
+    extra = dict(q_outlier_scale=10.0, k_outlier_scale=10.0) if outl == "peaky" else {}
     w = make_workload(400 + SMALL.index(case), lengths=lengths, num_q_heads=hq, num_kv_heads=hk, head_dim=d, g=g,
-                      route=route, p=p, kv_int8=kv8, blk_q=blk_q, outliers=outl)
+                      route=route, p=p, kv_int8=kv8, blk_q=blk_q, outliers=bool(outl), **extra)
     t = gp.prepare(w)
     out = gp.attn(w, t, out_fp32=True)
     out16 = gp.attn(w, t, out_fp32=False)

@@ -84,6 +84,14 @@ def fp32_inv_sqrt(d: int) -> float:
     return float(np.float32(1.0 / math.sqrt(d)))
 
 
+# Channel outliers: the same few channels are scaled up in K (strongly) and Q
+# (mildly), the pattern that makes per-block INT8 scales matter.  With these
+# defaults the scaled logits have a standard deviation of about 3.7 nats at
+# d = 128; q_scale = k_scale = 10 gives ~18 nats (near one-hot rows), used by
+# tests that stress the online-softmax rescaling.
+Q_OUTLIER_SCALE, K_OUTLIER_SCALE = 2.0, 10.0
+
+
 def _normal_fp16(rng: np.random.Generator, shape, outlier_channels=None, outlier_scale=10.0):
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if outlier_channels is not None and len(outlier_channels):
@@ -151,6 +159,7 @@ def route_bernoulli_tiles(cfg_id: int, num_kv_heads: int, lengths, T: int, p: fl
 def make_workload(cfg_id: int, *, lengths, num_q_heads: int, num_kv_heads: int, head_dim: int,
                   g: int, blk_q: int = 64, route: str = "bernoulli", p: float = 0.5,
                   outliers: bool = False, kv_int8: bool = False, max_seqlen: Optional[int] = None,
+                  q_outlier_scale: float = Q_OUTLIER_SCALE, k_outlier_scale: float = K_OUTLIER_SCALE,
                   name: str = "", notes: str = "") -> Workload:
     lengths = [int(x) for x in lengths]
     cu = cu_from_lengths(lengths)
@@ -158,8 +167,8 @@ def make_workload(cfg_id: int, *, lengths, num_q_heads: int, num_kv_heads: int, 
     max_seqlen = int(max_seqlen if max_seqlen is not None else max(lengths) if lengths else 1)
     T = (max_seqlen + TILE - 1) // TILE
     oc = outlier_channels(cfg_id, head_dim) if outliers else None
-    q = _normal_fp16(rng_for(cfg_id, S_Q), (N, num_q_heads, head_dim), oc)
-    k = _normal_fp16(rng_for(cfg_id, S_K), (N, num_kv_heads, head_dim), oc)
+    q = _normal_fp16(rng_for(cfg_id, S_Q), (N, num_q_heads, head_dim), oc, q_outlier_scale)
+    k = _normal_fp16(rng_for(cfg_id, S_K), (N, num_kv_heads, head_dim), oc, k_outlier_scale)
     v = _normal_fp16(rng_for(cfg_id, S_V), (N, num_kv_heads, head_dim), None)
     if route == "bernoulli":
         tr = route_bernoulli_groups(cfg_id, num_kv_heads, lengths, T, g, p)
