@@ -30,6 +30,23 @@ P_INT8 = 5033.2e12        # OP/s
 HBM_PEAK = 8.0e12         # B/s
 
 
+def measured_traffic(workload_name):
+    """HBM bytes per attention launch from the committed counter summary, if it was taken on this
+    workload with the attention kernel source as it is now (else None)."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", "attn_prefill_kernel_llama3b_B8_L4096_hbm_bytes.md")
+    src = os.path.join(ROOT, "mixed_precision_amd", "csrc", "attn_kernel.hpp")
+    if workload_name != "llama3.2-3b_attn_B8_L4096_h24kv8_d128_int8p75" or not os.path.exists(prof):
+        return None
+    text = open(prof).read()
+    h = re.search(r"source sha256: `([0-9a-f]{64})`", text)
+    t = re.search(r"roofline.traffic` = (\d+) bytes", text)
+    if not h or not t or h.group(1) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return int(t.group(1))
+
+
 def legal_pairs(lengths):
     return sum(L * (L + 1) // 2 for L in lengths)
 
@@ -111,6 +128,8 @@ def main():
     ap.add_argument("--p", type=float, default=None, help="INT8 coverage override (configs 2, 4, 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device a few times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
@@ -118,6 +137,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
     from mixed_precision_amd import tilemix as tm
     from workloads import config
 
@@ -150,12 +178,13 @@ def main():
         if w.kv_int8:
             tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
         tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
+        plan.schedule(cu, stream=stream)
         if ev is not None:
             ev[0].record(stream)
         if w.kv_int8:
-            plan.run(q, k_q, v_q, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream)
+            plan.run_planned(q, k_q, v_q, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream)
         else:
-            plan.run(q, k, v, q_q, q_s, k_q, k_s, cu, words, out, stream=stream)
+            plan.run_planned(q, k, v, q_q, q_s, k_q, k_s, cu, words, out, stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -184,8 +213,9 @@ def main():
                    "head_dim": d, "g": w.g, "blk_q": w.blk_q, "kv_int8": w.kv_int8,
                    "int8_pair_fraction": work["pairs_int8"] / work["pairs"], "tokens": N},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / blended_peak, "traffic": None,
-                     "kernel": "attn_prefill_kernel (+ work-list kernels)",
+                     "frac": achieved / blended_peak, "traffic": measured_traffic(w.name),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
+                     "kernel": "attn_prefill_kernel",
                      "note": "peak = blended MFMA peak of this launch's mix: ops / (F_qk16/P16 + F_qk8/P8 + F_pv/P16)"},
         "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
         "attn_tokens_per_s": N / t_attn, "t_star_ms": work["t_star"] * 1e3,

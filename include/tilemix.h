@@ -166,10 +166,33 @@ int32_t tilemix_attn_workspace_size(const tilemix_attn_params* params, size_t* b
  * acc / sum.  Key j is legal for query i iff j <= i < L_b (top-left causal).
  *
  * `workspace` must hold tilemix_attn_workspace_size() bytes (256-byte aligned);
- * it receives the varlen/GQA work list, rebuilt on every call.
+ * it receives the varlen/GQA work list, rebuilt on every call.  Equivalent to
+ * tilemix_attn_plan followed by tilemix_attn_run on the same stream.
  */
 int32_t tilemix_attn_prefill(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The varlen/GQA work schedule alone ([PL §4]: prefix-sum metadata,
+ * padding-free execution): from cu_seqlens (device int32 [batch+1]) it writes
+ * the work list of (sequence, KV head, query tile, head chunk) items into
+ * `workspace`, longest causal rows first, each (sequence, KV head) group kept
+ * on one XCD where the slots allow.  Asynchronous on `stream`; no allocation.
+ * The list depends only on `params` and cu_seqlens, so several layers of one
+ * batch may share it.
+ */
+int32_t tilemix_attn_plan(const tilemix_attn_params* params, const int32_t* cu_seqlens, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * The attention of tilemix_attn_prefill over the work list a previous
+ * tilemix_attn_plan wrote into `workspace` (same params, same cu_seqlens
+ * contents, ordered before this call on the stream).  Items whose indices fall
+ * outside the problem are skipped, so a stale or missing list gives wrong
+ * output, never an out-of-range access.
+ */
+int32_t tilemix_attn_run(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Host struct: debug products of tilemix_attn_prefill_debug (device pointers, any may be NULL). */
 typedef struct {

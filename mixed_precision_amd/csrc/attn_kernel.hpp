@@ -343,10 +343,12 @@ void attn_prefill_kernel(const AttnArgs a) {
 
   const WorkItem item = a.items[blockIdx.x];
   const int b = uniform(item.b);
-  if (b < 0) return;
   const int hk = uniform(item.hk);
   const int m = uniform(item.m);
   const int chunk = uniform(item.chunk);
+  // empty slot (b < 0), or an item outside the problem (work list not built
+  // for these parameters): nothing to do
+  if (b < 0 || b >= a.batch || hk < 0 || hk >= a.Hk || m < 0 || m >= a.T || chunk < 0 || chunk >= a.nch) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -129,12 +129,19 @@ int32_t validate_tensors(const tilemix_attn_params* p, const tilemix_attn_tensor
   return TILEMIX_OK;
 }
 
-int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t, void* workspace,
-                    size_t workspace_bytes, const tilemix_debug* dbg, hipStream_t stream) {
+enum class Mode { kPlanAndRun, kPlanOnly, kRunOnly };
+
+int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t, const int32_t* cu_seqlens,
+                    void* workspace, size_t workspace_bytes, const tilemix_debug* dbg, hipStream_t stream, Mode mode) {
   int32_t st = validate_attn_params(p);
   if (st != TILEMIX_OK) return st;
-  st = validate_tensors(p, t);
-  if (st != TILEMIX_OK) return st;
+  if (mode != Mode::kPlanOnly) {
+    st = validate_tensors(p, t);
+    if (st != TILEMIX_OK) return st;
+    cu_seqlens = t->cu_seqlens;
+  } else if (!cu_seqlens || !aligned(cu_seqlens, 4)) {
+    return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens must be a non-NULL, 4-byte aligned device pointer");
+  }
   const Derived d = derive(p);
   if (!workspace || workspace_bytes < d.ws.total)
     return fail(TILEMIX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", d.ws.total, workspace_bytes,
@@ -152,7 +159,7 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
 
   char* ws = static_cast<char*>(workspace);
   SchedArgs sa;
-  sa.cu = t->cu_seqlens;
+  sa.cu = cu_seqlens;
   sa.batch = p->batch;
   sa.T = d.T;
   sa.Hk = p->num_kv_heads;
@@ -170,8 +177,12 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
   sa.seg = reinterpret_cast<int32_t*>(ws + d.ws.seg_off);
   sa.segidx = reinterpret_cast<int32_t*>(ws + d.ws.segidx_off);
   sa.order = reinterpret_cast<int32_t*>(ws + d.ws.order_off);
-  hipError_t e = launch_schedule(sa, stream);
-  if (e != hipSuccess) return hip_status(e, "work-list launch");
+  hipError_t e = hipSuccess;
+  if (mode != Mode::kRunOnly) {
+    e = launch_schedule(sa, stream);
+    if (e != hipSuccess) return hip_status(e, "work-list launch");
+    if (mode == Mode::kPlanOnly) return ok();
+  }
 
   AttnArgs a{};
   a.q = t->q;
@@ -360,13 +371,27 @@ int32_t tilemix_attn_workspace_size(const tilemix_attn_params* params, size_t* b
 
 int32_t tilemix_attn_prefill(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  return attn_common(params, tensors, workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream));
+  return attn_common(params, tensors, nullptr, workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream),
+                     Mode::kPlanAndRun);
+}
+
+int32_t tilemix_attn_plan(const tilemix_attn_params* params, const int32_t* cu_seqlens, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return attn_common(params, nullptr, cu_seqlens, workspace, workspace_bytes, nullptr,
+                     static_cast<hipStream_t>(stream), Mode::kPlanOnly);
+}
+
+int32_t tilemix_attn_run(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return attn_common(params, tensors, nullptr, workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream),
+                     Mode::kRunOnly);
 }
 
 int32_t tilemix_attn_prefill_debug(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors,
                                    void* workspace, size_t workspace_bytes, const tilemix_debug* dbg, void* stream) {
   if (!dbg) return fail(TILEMIX_ERR_INVALID_ARG, "dbg is NULL");
-  return attn_common(params, tensors, workspace, workspace_bytes, dbg, static_cast<hipStream_t>(stream));
+  return attn_common(params, tensors, nullptr, workspace, workspace_bytes, dbg, static_cast<hipStream_t>(stream),
+                     Mode::kPlanAndRun);
 }
 
 }  // extern "C"

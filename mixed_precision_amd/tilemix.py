@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "TILEMIX_OK", 1: "TILEMIX_ERR_INVALID_ARG", 2: "TILEMIX_ERR_U
 # Every symbol include/tilemix.h declares.
 EXPORTED = ("tilemix_status_string", "tilemix_last_error", "tilemix_version", "tilemix_quantize_blockwise",
             "tilemix_build_route_mask", "tilemix_decode_route_mask", "tilemix_attn_workspace_size",
-            "tilemix_attn_prefill", "tilemix_attn_prefill_debug")
+            "tilemix_attn_prefill", "tilemix_attn_plan", "tilemix_attn_run", "tilemix_attn_prefill_debug")
 
 
 class TilemixError(RuntimeError):
@@ -79,6 +79,10 @@ def _load():
     lib.tilemix_attn_workspace_size.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(sz)]
     lib.tilemix_attn_prefill.restype = i32
     lib.tilemix_attn_prefill.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(AttnTensors), vp, sz, vp]
+    lib.tilemix_attn_plan.restype = i32
+    lib.tilemix_attn_plan.argtypes = [ctypes.POINTER(AttnParams), vp, vp, sz, vp]
+    lib.tilemix_attn_run.restype = i32
+    lib.tilemix_attn_run.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(AttnTensors), vp, sz, vp]
     lib.tilemix_attn_prefill_debug.restype = i32
     lib.tilemix_attn_prefill_debug.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(AttnTensors), vp, sz,
                                                ctypes.POINTER(Debug), vp]
@@ -212,8 +216,22 @@ class AttnPlan:
         self.ws_bytes = tilemix_attn_workspace_size(problem)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
 
+    def schedule(self, cu_seqlens, stream=None):
+        """tilemix_attn_plan: build the work list for `cu_seqlens` into the workspace."""
+        _check(_lib.tilemix_attn_plan(ctypes.byref(self.params), _ptr(cu_seqlens), _ptr(self.workspace),
+                                      self.ws_bytes, _stream(stream)))
+
+    def run_planned(self, q, k, v, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, out, v_scale=None,
+                    stream=None):
+        """tilemix_attn_run: attention over the work list a previous schedule() built."""
+        t = _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out)
+        _check(_lib.tilemix_attn_run(ctypes.byref(self.params), ctypes.byref(t), _ptr(self.workspace),
+                                     self.ws_bytes, _stream(stream)))
+        return out
+
     def run(self, q, k, v, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, out, v_scale=None,
             debug: Optional[Debug] = None, stream=None):
+        """tilemix_attn_prefill (work list + attention), or its debug variant."""
         t = _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out)
         if debug is None:
             st = _lib.tilemix_attn_prefill(ctypes.byref(self.params), ctypes.byref(t), _ptr(self.workspace),

@@ -33,8 +33,8 @@ def header_functions():
 def test_header_declares_expected_calls():
     names = header_functions()
     for n in ("tilemix_quantize_blockwise", "tilemix_build_route_mask", "tilemix_decode_route_mask",
-              "tilemix_attn_workspace_size", "tilemix_attn_prefill", "tilemix_attn_prefill_debug",
-              "tilemix_status_string", "tilemix_last_error"):
+              "tilemix_attn_workspace_size", "tilemix_attn_prefill", "tilemix_attn_plan", "tilemix_attn_run",
+              "tilemix_attn_prefill_debug", "tilemix_status_string", "tilemix_last_error"):
         assert n in names
 
 
@@ -97,6 +97,13 @@ def test_null_pointer_and_workspace_errors(tm):
     assert lib.tilemix_attn_prefill(ctypes.byref(pc), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 2
     assert lib.tilemix_attn_prefill_debug(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None,
                                           None) == 1
+    # plan / run split: same validation, before any launch
+    assert lib.tilemix_attn_plan(ctypes.byref(p), None, ctypes.c_void_p(a), 1 << 30, None) == 1
+    assert lib.tilemix_attn_plan(ctypes.byref(p), ctypes.c_void_p(a), None, 0, None) == 4
+    assert lib.tilemix_attn_plan(ctypes.byref(pc), ctypes.c_void_p(a), ctypes.c_void_p(a), 1 << 30, None) == 2
+    assert lib.tilemix_attn_run(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 4
+    t.q_stride_tok = 24 * 128 + 3
+    assert lib.tilemix_attn_run(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 1
 
 
 def test_quantize_and_route_validation(tm):
