@@ -55,10 +55,6 @@
 #include "device_common.hpp"
 #include "internal.hpp"
 
-#ifndef TM_SETPRIO
-#define TM_SETPRIO 3
-#endif
-
 namespace tilemix {
 
 
@@ -337,9 +333,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_kernel(const AttnArgs a) {
   using A = Attn<D, QB, KVI8>;
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
-  __shared__ __attribute__((aligned(1024))) char smem[A::LDS_BYTES];
-  auto kbuf = [&](int i) -> char* { return smem + i * A::KBYTES; };                   // i in 0..1
-  auto vbuf = [&](int i) -> char* { return smem + 2 * A::KBYTES + i * A::VBYTES; };   // i in 0..1
+  // two stages (K tile, then V tile) as two LDS objects: with a fixed object
+  // per access the compiler can tell the loads into one stage from reads of
+  // the other and does not make those reads wait for the loads
+  __shared__ __attribute__((aligned(1024))) char stA[A::KBYTES + A::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char stB[A::KBYTES + A::VBYTES];
 
   const WorkItem item = a.items[blockIdx.x];
   const int b = uniform(item.b);
@@ -352,7 +350,7 @@ void attn_prefill_kernel(const AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int c = lane & 15;           // query column / operand row inside a 16-block
   const int gq = lane >> 4;          // lane group 0..3
   const int seq0 = uniform(a.cu[b]);
@@ -403,8 +401,9 @@ void attn_prefill_kernel(const AttnArgs a) {
   const uint32_t kv_stride = (uint32_t)(a.kv_st * esz);
   const uint32_t k8_stride = KVI8 ? kv_stride : (uint32_t)(a.Hk * D);
   const char* k8base = KVI8 ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)seq0 * a.Hk + hk) * D);
-  auto tile_rsrc = [&](const char* base, uint32_t stride, int n) {
-    const int rows = max(L - n * kTile, 0);
+  // (empty: a zero-length range, the load reads zeros and touches no memory)
+  auto tile_rsrc = [&](const char* base, uint32_t stride, int n, bool empty) __attribute__((always_inline)) {
+    const int rows = empty ? 0 : max(L - n * kTile, 0);
     return make_rsrc(base + (int64_t)n * kTile * stride, (uint32_t)rows * stride);
   };
   typename A::Dma dma;
@@ -412,19 +411,25 @@ void attn_prefill_kernel(const AttnArgs a) {
 
   const uint64_t word = uniform64(a.words[((int64_t)hk * a.batch + b) * a.T + m]);
   const int g = a.g;
-  const float* kscale_row = a.k_scale + ((int64_t)hk * a.batch + b) * a.T;
-  const float* vscale_row = KVI8 ? a.v_scale + ((int64_t)hk * a.batch + b) * a.T : nullptr;
+  // per-tile scales through the scalar cache (a vector load would be counted
+  // behind the tile loads in flight, and waiting for it would wait for them)
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* kscale_row = (cfloat*)(a.k_scale + ((int64_t)hk * a.batch + b) * a.T);
+  cfloat* vscale_row = KVI8 ? (cfloat*)(a.v_scale + ((int64_t)hk * a.batch + b) * a.T) : nullptr;
   // Route of tile n = bit floor(n/g) of the word, tracked incrementally:
   // bit 0 of wsh is the current tile's group, `left` counts the tiles the
   // group still covers (groups past bit 63 shift in zeros = FP16).
   uint64_t wsh = word;
   int left = g;
-  auto fetch = [&](int n, int route, typename A::Stage& st) {     // start the loads of tile n
+  // start the loads of tile n (K in its route's form, and V) into stage `sg`
+  auto fetch = [&](int n, int route, typename A::Stage& st, char* sg, bool empty) __attribute__((always_inline)) {
     if (KVI8) {
-      A::stage_load(st, tid, tile_rsrc(kbase, kv_stride, n), tile_rsrc(vbase, kv_stride, n), kv_stride);
+      A::stage_load(st, tid, tile_rsrc(kbase, kv_stride, n, empty), tile_rsrc(vbase, kv_stride, n, empty),
+                    kv_stride);
     } else {
-      A::dma_tile(route, wave, dma, kv_stride, k8_stride, tile_rsrc(kbase, kv_stride, n),
-                  tile_rsrc(k8base, k8_stride, n), tile_rsrc(vbase, kv_stride, n), kbuf(n & 1), vbuf(n & 1));
+      A::dma_tile(route, wave, dma, kv_stride, k8_stride, tile_rsrc(kbase, kv_stride, n, empty),
+                  tile_rsrc(k8base, k8_stride, n, empty), tile_rsrc(vbase, kv_stride, n, empty), sg,
+                  sg + A::KBYTES);
     }
   };
 
@@ -442,24 +447,29 @@ void attn_prefill_kernel(const AttnArgs a) {
   // ---- prologue: tile 0 into stage 0
   {
     typename A::Stage st;
-    fetch(0, (int)(wsh & 1), st);
-    if (KVI8) A::stage_store(st, (int)(wsh & 1), tid, kbuf(0), vbuf(0));
+    fetch(0, (int)(wsh & 1), st, stA, false);
+    if (KVI8) {
+      wait_vmem();
+      A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES);
+    }
   }
   wait_vmem();
   __syncthreads();
 
-  // Tile n: tile n+1's loads are issued first (into stage (n+1)%2, last read
-  // in step n-1), then tile n is computed from stage n%2 in two 32-key halves.
-  // One loop body serves every tile; only the QK^T path and the diagonal mask
-  // branch (uniformly) inside it.
-  for (int n = 0; n <= m; ++n) {
+  // Tile n: tile n+1's loads are issued first (into the other stage, last
+  // read in step n-1; after the last tile they read nothing), then tile n is
+  // computed from its stage in two 32-key halves, and the loads are awaited
+  // before the barrier.  One body serves every tile; only the QK^T path and
+  // the diagonal mask branch (uniformly) inside it.  The loop runs two tiles
+  // per iteration so each stage is a fixed LDS object.
+  auto tile = [&](int n, const char* cur, char* next) __attribute__((always_inline)) {
     const int rc = (int)(wsh & 1);
     const int rnext = (left == 1) ? (int)((wsh >> 1) & 1) : rc;
     const bool last = (n == m);
-    const char* kl = kbuf(n & 1);
-    const char* vl = vbuf(n & 1);
+    const char* kl = cur;
+    const char* vl = cur + A::KBYTES;
     typename A::Stage st;
-    if (!last) fetch(n + 1, rnext, st);
+    fetch(n + 1, rnext, st, next, last);
     const float ksc = kscale_row[n];
     float cj[QB];
 #pragma unroll
@@ -483,7 +493,9 @@ void attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       i32x4 S[QB][2];
-      if (TM_SETPRIO & 1) __builtin_amdgcn_s_setprio(1);
+      // a wave issuing MFMAs gets priority, so the other wave of the SIMD runs
+      // its softmax in their shadow
+      __builtin_amdgcn_s_setprio(1);
       if (rc == 0) {
         A::qk16(kl, h, qf, S, c, gq);
       } else {
@@ -507,22 +519,30 @@ void attn_prefill_kernel(const AttnArgs a) {
         for (int j = 0; j < QB; ++j) qpos[j] = m * kTile + qb_row(j);
         A::mask_diag(S, n * kTile + 32 * h + 4 * gq, qpos);
       }
-      if (TM_SETPRIO & 1) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
       f16x8 P[QB];
       A::softmax(S, cj, vsc, mref, lrow, O, P);
-      if (TM_SETPRIO & 2) __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(1);
       A::pv(vl, h, P, O, lane);
-      if (TM_SETPRIO & 2) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
     }
-    if (!last) {
-      if (KVI8) A::stage_store(st, rnext, tid, kbuf((n + 1) & 1), vbuf((n + 1) & 1));
+    if (KVI8) {
       wait_vmem();
-      __syncthreads();
+      A::stage_store(st, rnext, tid, next, next + A::KBYTES);
     }
+    wait_vmem();
+    __syncthreads();
     if (--left == 0) {
       left = g;
       wsh >>= 1;
     }
+  };
+#pragma unroll 1
+  for (int n = 0;; n += 2) {
+    tile(n, stA, stB);
+    if (n + 1 > m) break;
+    tile(n + 1, stB, stA);
+    if (n + 2 > m) break;
   }
 
   // ---- epilogue: O = acc / l
