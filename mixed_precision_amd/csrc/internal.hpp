@@ -70,7 +70,7 @@ struct AttnArgs {
 struct SchedArgs {
   const int32_t* cu;
   int32_t batch, T, Hk, nch;
-  int32_t cost_shift;   // group costs >> cost_shift keep every XCD load below 2^31
+  int32_t cost_shift;   // group costs >> cost_shift keep every XCD load below 2^28
   int64_t nslots, segmax;
   WorkItem* items;
   int32_t* seg;      // int32 [segmax][6]: xcd, slot_begin, count, item_begin, b, hk

@@ -9,34 +9,38 @@
 //
 // The packer takes per-tile decisions; a group's bit is the AND of its legal
 // tiles (FP16 wins on disagreement) and bits of groups without a legal tile are
-// 0, so equal decisions give equal words.  Both kernels are tiny (one thread
-// per word or per tile) and run once per routing template.
+// 0, so equal decisions give equal words.  Both kernels are tiny (one wave per
+// word, one thread per tile) and run once per routing template.
 #include "device_common.hpp"
 #include "internal.hpp"
 
 namespace tilemix {
 
+// One wavefront per word: lane j reduces group j (key tiles j*g .. j*g+g-1 up to
+// the row's last legal tile m; at most 64 groups per word) and a ballot packs the
+// 64 group bits.
 __global__ __launch_bounds__(256) void build_route_kernel(RouteArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // word [hk][b][m]
+  const int lane = threadIdx.x & 63;
   const int64_t total = (int64_t)a.num_kv_heads * a.batch * a.T;
   if (idx >= total) return;
   const int m = (int)(idx % a.T);
   const int b = (int)((idx / a.T) % a.batch);
   const int L = a.cu[b + 1] - a.cu[b];
   const int Tb = (L + kTile - 1) / kTile;
-  uint64_t w = 0;
+  bool bit = false;
   if (m < Tb) {
     const uint8_t* row = a.tile_route + idx * a.T;   // [hk][b][m][:]
-    bool all = true;
-    for (int n = 0; n <= m; ++n) {
-      all = all && (row[n] != 0);
-      if ((n + 1) % a.g == 0 || n == m) {
-        if (all) w |= 1ull << (n / a.g);
-        all = true;
-      }
+    const int n0 = lane * a.g;
+    const int n1 = min(n0 + a.g, m + 1);
+    if (n0 < n1) {                                   // the group has a legal tile: AND over them
+      bool all = true;
+      for (int n = n0; n < n1; ++n) all = all && (row[n] != 0);
+      bit = all;
     }
   }
-  a.words_out[idx] = w;
+  const uint64_t w = __ballot(bit);
+  if (lane == 0) a.words_out[idx] = w;
 }
 
 __global__ __launch_bounds__(256) void decode_route_kernel(RouteArgs a) {
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(256) void decode_route_kernel(RouteArgs a) {
 
 hipError_t launch_build_route(const RouteArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.num_kv_heads * a.batch * a.T;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const unsigned blocks = (unsigned)((total + 3) / 4);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(build_route_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();

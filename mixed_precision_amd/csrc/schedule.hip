@@ -21,9 +21,8 @@
 //
 // plan: one workgroup.  Tile counts and the rank sort live in LDS (global
 //   scratch past kPlanLdsBatch sequences); the greedy placement runs in wave 0
-//   as wave-uniform 32-bit scalar code and writes each segment to the segment
-//   table without reading it back, then the segment count and per-XCD fill
-//   levels.
+//   with one XCD per lane and writes each segment to the segment table without
+//   reading it back, then the segment count and per-XCD fill levels.
 // emit: one workgroup per segment writes that segment's items; 8 more
 //   workgroups mark each XCD's unused slots empty (b = -1).
 #include "device_common.hpp"
@@ -32,7 +31,20 @@
 namespace tilemix {
 
 namespace {
-constexpr int kSegFields = 6;           // xcd, slot_begin, count, item_begin, b, hk
+constexpr int kSegFields = 6;
+// min / max over each group of 8 lanes (all 8 end with the result)
+TM_DEV uint32_t min8(uint32_t k) {
+  k = min(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  k = min(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  k = min(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  return k;
+}
+TM_DEV uint32_t max8(uint32_t k) {
+  k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0xB1, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x4E, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x141, 0xF, 0xF, false));
+  return k;
+}           // xcd, slot_begin, count, item_begin, b, hk
 constexpr int kPlanLdsBatch = 4096;     // sequences whose tile counts / order fit in LDS
 }  // namespace
 
@@ -58,15 +70,14 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
   __syncthreads();
   if (threadIdx.x >= 64) return;
 
-  // 2) greedy placement of (b, hk) groups on XCDs.  Every value is
-  //    wave-uniform and 32-bit (scalar ALU); the per-XCD state is indexed with
-  //    compile-time indices only.  Costs are shifted right by cost_shift so
-  //    the largest possible XCD load fits in 31 bits.
+  // 2) greedy placement of (b, hk) groups on XCDs, by wave 0: lane x < 8
+  //    holds XCD x's used slots and load; the least-loaded XCD with room is a
+  //    min over 8 lanes of (load << 3 | x) (DPP quad swaps and a half-row
+  //    mirror), so each placement is a few instructions with no memory trip.
+  //    Costs are shifted right by cost_shift so loads stay below 2^28.
   const int lane = threadIdx.x;
   const uint32_t cap = (uint32_t)(a.nslots / kNumXcd);
-  uint32_t used[kNumXcd], load[kNumXcd];
-#pragma unroll
-  for (int x = 0; x < kNumXcd; ++x) used[x] = load[x] = 0;
+  uint32_t used = 0, load = 0;
   uint32_t nseg = 0;
   const uint32_t segmax = (uint32_t)a.segmax;
   for (int r = 0; r < a.batch; ++r) {
@@ -78,30 +89,21 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
     for (int hk = 0; hk < a.Hk; ++hk) {
       uint32_t remaining = cnt, ib = 0;
       while (remaining > 0 && nseg < segmax) {
-        int best = -1;
-        uint32_t best_load = 0;
-#pragma unroll
-        for (int x = 0; x < kNumXcd; ++x) {
-          const bool pick = (cap - used[x] >= remaining) && (best < 0 || load[x] < best_load);
-          best = pick ? x : best;
-          best_load = pick ? load[x] : best_load;
-        }
-        uint32_t take = remaining;
-        if (best < 0) {                           // split: XCD with the most free slots
-          best = 0;
-          uint32_t best_free = cap - used[0];
-#pragma unroll
-          for (int x = 1; x < kNumXcd; ++x) {
-            const bool pick = cap - used[x] > best_free;
-            best = pick ? x : best;
-            best_free = pick ? cap - used[x] : best_free;
-          }
-          take = best_free;
+        const bool fits = lane < kNumXcd && cap - used >= remaining;
+        const uint32_t kmin = uniform(min8(fits ? (load << 3) | (uint32_t)lane : 0xFFFFFFFFu));
+        int best;
+        uint32_t take;
+        if (kmin != 0xFFFFFFFFu) {
+          best = (int)(kmin & 7u);
+          take = remaining;
+        } else {                                  // split: XCD with the most free slots (lowest index on ties)
+          const uint32_t kmax =
+              uniform(max8(lane < kNumXcd ? ((cap - used) << 3) | (uint32_t)(7 - lane) : 0u));
+          best = 7 - (int)(kmax & 7u);
+          take = kmax >> 3;
           if (take == 0) break;                   // cannot happen: slots >= items
         }
-        uint32_t slot_begin = 0;
-#pragma unroll
-        for (int x = 0; x < kNumXcd; ++x) slot_begin = (x == best) ? used[x] : slot_begin;
+        const uint32_t slot_begin = (uint32_t)__builtin_amdgcn_readlane((int)used, best);
         if (lane == 0) {
           int32_t* sg = a.seg + (int64_t)nseg * kSegFields;
           sg[0] = best;
@@ -112,10 +114,9 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
           sg[5] = hk;
         }
         const uint32_t add = (take == cnt) ? cost : (uint32_t)((uint64_t)cost * take / cnt);
-#pragma unroll
-        for (int x = 0; x < kNumXcd; ++x) {
-          used[x] += (x == best) ? take : 0u;
-          load[x] += (x == best) ? add : 0u;
+        if (lane == best) {
+          used += take;
+          load += add;
         }
         ++nseg;
         ib += take;
@@ -123,11 +124,8 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
       }
     }
   }
-  if (lane == 0) {
-    a.segidx[0] = (int32_t)nseg;
-#pragma unroll
-    for (int x = 0; x < kNumXcd; ++x) a.segidx[1 + x] = (int32_t)used[x];
-  }
+  if (lane == 0) a.segidx[0] = (int32_t)nseg;
+  if (lane < kNumXcd) a.segidx[1 + lane] = (int32_t)used;
 }
 
 __global__ __launch_bounds__(256) void schedule_emit_kernel(SchedArgs a) {

@@ -168,7 +168,7 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
     // upper bound of the summed cost of all groups: every sequence at T tiles
     const uint64_t total = (uint64_t)p->batch * p->num_kv_heads * d.nch * (uint64_t)d.T * (d.T + 1) / 2;
     int shift = 0;
-    while ((total >> shift) >= ((uint64_t)1 << 31)) ++shift;
+    while ((total >> shift) >= ((uint64_t)1 << 28)) ++shift;
     sa.cost_shift = shift;
   }
   sa.nslots = d.ws.nslots;

@@ -143,7 +143,10 @@ def tilemix_quantize_blockwise(x: torch.Tensor, cu_seqlens: torch.Tensor, max_se
         x_q = torch.empty((N, H, d), dtype=torch.int8, device=x.device)
     if scales is None:
         scales = torch.empty((H, B, nb), dtype=torch.float32, device=x.device)
-    _check(_lib.tilemix_quantize_blockwise(_ptr(x), x.stride(0), x.stride(1), _ptr(cu_seqlens), B, int(max_seqlen),
+    # the stride of a size-1 dimension never addresses anything (it can be 0 on views)
+    st_tok = x.stride(0) if N > 1 else H * d
+    st_head = x.stride(1) if H > 1 else d
+    _check(_lib.tilemix_quantize_blockwise(_ptr(x), st_tok, st_head, _ptr(cu_seqlens), B, int(max_seqlen),
                                            H, d, int(blk), _ptr(x_q), _ptr(scales), _stream(stream)))
     return x_q, scales
 
@@ -201,7 +204,11 @@ def tilemix_attn_workspace_size(problem: AttnProblem) -> int:
 def _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out) -> AttnTensors:
     if q.stride(2) != 1 or k.stride(2) != 1 or v.stride(2) != 1 or k.stride() != v.stride():
         raise ValueError("q/k/v channels must be contiguous and k, v must share strides")
-    return AttnTensors(q.data_ptr(), k.data_ptr(), v.data_ptr(), q.stride(0), q.stride(1), k.stride(0), k.stride(1),
+    def st(t, dim):   # the stride of a size-1 dimension never addresses anything (it can be 0 on views)
+        if t.shape[dim] > 1:
+            return t.stride(dim)
+        return t.shape[2] * (t.shape[1] if dim == 0 else 1)
+    return AttnTensors(q.data_ptr(), k.data_ptr(), v.data_ptr(), st(q, 0), st(q, 1), st(k, 0), st(k, 1),
                        q_q.data_ptr(), q_scale.data_ptr(), None if k_q is None else k_q.data_ptr(),
                        k_scale.data_ptr(), None if v_scale is None else v_scale.data_ptr(), cu_seqlens.data_ptr(),
                        route_words.data_ptr(), out.data_ptr())

@@ -57,6 +57,46 @@ def test_quantize_bitexact(gp, name, shape, blk):
     assert np.array_equal(qs.cpu().numpy().view(np.uint32), rs.view(np.uint32))
 
 
+def _edge_blocks(rng):
+    """64 x 128 fp16 blocks that stress the quantiser's rounding: exact half-way
+    quotients (ties to even) at several power-of-two scales, subnormal-only
+    blocks, the largest fp16 magnitude, an all-zero block, all-ones mantissas."""
+    blocks = []
+    for e in (-14, -10, -3, 0, 2, 8):
+        k = rng.integers(-127, 127, size=(64, 128))
+        b = ((k + 0.5) * 2.0 ** e).astype(np.float64)
+        b[0, 0] = 127 * 2.0 ** e                        # amax = 127 * 2^e -> scale 2^e exactly
+        blocks.append(b)
+    sub = rng.integers(-1023, 1024, size=(64, 128)) * 2.0 ** -24   # fp16 subnormals
+    blocks.append(sub)
+    big = rng.standard_normal((64, 128)) * 1000.0
+    big[5, 7] = -65504.0
+    blocks.append(big)
+    blocks.append(np.zeros((64, 128)))
+    ones = rng.uniform(-1, 1, size=(64, 128)) * (2047 / 1024) * 2.0 ** 5
+    ones[3, 3] = (2047 / 1024) * 2.0 ** 5
+    blocks.append(ones)
+    for _ in range(6):
+        m = rng.integers(-14, 15)
+        blocks.append(rng.standard_normal((64, 128)) * 2.0 ** m)
+    return np.concatenate(blocks).astype(np.float16)[:, None, :]
+
+
+def test_quantize_edge_cases_bitexact(gp):
+    import torch
+    _announce("quantize edge cases")
+    rng = np.random.default_rng(77)
+    x = _edge_blocks(rng)
+    N = x.shape[0]
+    cu = np.array([0, N], dtype=np.int32)
+    xd = torch.from_numpy(x).cuda()
+    qq, qs = gp.tm.tilemix_quantize_blockwise(xd, torch.from_numpy(cu).cuda(), N, 64)
+    torch.cuda.synchronize()
+    rq, rs = orc.quantize_blockwise(x, cu, N, 64)
+    assert np.array_equal(qs.cpu().numpy(), rs)
+    assert np.array_equal(qq.cpu().numpy(), rq)
+
+
 def test_quantize_strided_input(gp):
     """Q as a view into a packed QKV buffer (token stride > heads*d)."""
     import torch
