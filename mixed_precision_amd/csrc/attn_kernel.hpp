@@ -363,13 +363,15 @@ void attn_prefill_kernel(const AttnArgs a) {
   auto qb_head = [&](int j) { return hk * a.G + h_begin + ((wave * nh + j) >> 2); };
   auto qb_row = [&](int j) { return qb_rb(j) * 16 + c; };                           // query offset in tile
   auto qb_valid = [&](int j) { return (j < nh) && (m * kTile + qb_row(j) < L); };
-  float sq[QB];
+  // q-block scale times sm_scale * log2(e): the INT8 score factor is sqs * k_scale
+  float sqs[QB];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     const int blk_start = m * kTile + qb_rb(j) * 16;
-    sq[j] = 1.0f;
+    float sq = 1.0f;
     if (j < nh && blk_start < L)
-      sq[j] = a.q_scale[((int64_t)qb_head(j) * a.batch + b) * a.nbq + blk_start / a.blk_q];
+      sq = a.q_scale[((int64_t)qb_head(j) * a.batch + b) * a.nbq + blk_start / a.blk_q];
+    sqs[j] = sq * a.sm_log2;
   }
 
   // ---- Q operands (B = Q^T): fp16 and int8, loaded once
@@ -471,12 +473,16 @@ void attn_prefill_kernel(const AttnArgs a) {
     typename A::Stage st;
     fetch(n + 1, rnext, st, next, last);
     const float ksc = kscale_row[n];
+    // score factors, kept > 0 so a (caller-supplied) zero scale cannot turn a
+    // masked -inf into NaN
     float cj[QB];
+    if (rc) {
 #pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      // kept > 0 so a (caller-supplied) zero scale cannot turn a masked -inf into NaN
-      cj[j] = rc ? sq[j] * ksc * a.sm_log2 : (KVI8 ? ksc * a.sm_log2 : a.sm_log2);
-      cj[j] = __builtin_elementwise_maximum(cj[j], 1.17549435e-38f);
+      for (int j = 0; j < QB; ++j) cj[j] = __builtin_elementwise_maximum(sqs[j] * ksc, 1.17549435e-38f);
+    } else {
+      const float c16 = __builtin_elementwise_maximum(KVI8 ? ksc * a.sm_log2 : a.sm_log2, 1.17549435e-38f);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) cj[j] = c16;
     }
     const float vsc = KVI8 ? vscale_row[n] : 1.0f;
     if (DBG) {
