@@ -3,7 +3,8 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: blockwise INT8 quantisation of Q and K (and V for the
 INT8 KV cache), route-word packing, the varlen/GQA work list and the fused
-attention kernel.  Default workload: the LLaMA-3.2-3B-shaped attention layer
+attention kernel.  With --otf the quantiser calls drop out and the attention
+kernel makes the INT8 operands on chip.  Default workload: the LLaMA-3.2-3B-shaped attention layer
 (batch 8, L = 4096, 24 query / 8 KV heads, d = 128, causal, FP16, 4 outlier
 channels, 64x64 tiles, g = 1, 75 % of the legal tile groups INT8).
 
@@ -126,6 +127,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--p", type=float, default=None, help="INT8 coverage override (configs 2, 4, 5)")
+    ap.add_argument("--otf", action="store_true",
+                    help="on-the-fly quantisation: Q/K INT8 operands made inside the attention kernel "
+                         "(no quantiser calls in the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -157,7 +161,11 @@ def main():
     N, Hq, d = w.q.shape
     Hk = w.num_kv_heads
     B = w.batch
-    plan = tm.AttnPlan(tm.AttnProblem(B, w.max_seqlen, Hq, Hk, d, w.g, w.blk_q, w.sm_scale, w.kv_int8, False), dev)
+    if args.otf and w.kv_int8:
+        print("--otf applies to an fp16 K/V workload", file=sys.stderr)
+        sys.exit(2)
+    plan = tm.AttnPlan(tm.AttnProblem(B, w.max_seqlen, Hq, Hk, d, w.g, w.blk_q, w.sm_scale, w.kv_int8, False,
+                                      args.otf), dev)
     nbq = (w.max_seqlen + w.blk_q - 1) // w.blk_q
     T = w.T
     q_q = torch.empty((N, Hq, d), dtype=torch.int8, device=dev)
@@ -173,8 +181,9 @@ def main():
     work = work_model(w, words.cpu().numpy().view(np.uint64))
 
     def step(ev=None):
-        tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
-        tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
+        if not args.otf:
+            tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
+            tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
         if w.kv_int8:
             tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
         tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
@@ -183,6 +192,8 @@ def main():
             ev[0].record(stream)
         if w.kv_int8:
             plan.run_planned(q, k_q, v_q, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream)
+        elif args.otf:
+            plan.run_planned(q, k, v, None, None, None, None, cu, words, out, stream=stream)
         else:
             plan.run_planned(q, k, v, q_q, q_s, k_q, k_s, cu, words, out, stream=stream)
         if ev is not None:
@@ -211,9 +222,10 @@ def main():
         "dtype": "fp16+int8 (fp32 accumulation / int32 accumulation)", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": w.max_seqlen, "num_q_heads": Hq, "num_kv_heads": Hk,
                    "head_dim": d, "g": w.g, "blk_q": w.blk_q, "kv_int8": w.kv_int8,
+                   "operands": "on-the-fly" if args.otf else "quantize-once",
                    "int8_pair_fraction": work["pairs_int8"] / work["pairs"], "tokens": N},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / blended_peak, "traffic": measured_traffic(w.name),
+                     "frac": achieved / blended_peak, "traffic": None if args.otf else measured_traffic(w.name),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "kernel": "attn_prefill_kernel",
                      "note": "peak = blended MFMA peak of this launch's mix: ops / (F_qk16/P16 + F_qk8/P8 + F_pv/P16)"},

@@ -126,6 +126,13 @@ typedef struct {
   int32_t causal;       /* must be 1 */
   int32_t kv_int8;      /* 0: k, v are fp16; 1: k, v are an INT8 cache with scales */
   int32_t out_fp32;     /* 0: out is fp16; 1: out is float32 */
+  int32_t otf_quant;    /* 0: quantise-once operands (q_q, q_scale, k_q, k_scale from
+                           tilemix_quantize_blockwise); 1: on-the-fly quantisation
+                           ([PL App. C], [PL App. D]): the kernel derives the block scales
+                           and INT8 fragments of Q and of INT8-routed K tiles on chip from
+                           q and k, with the same definition and bit-identical results;
+                           q_q, q_scale, k_q and k_scale are not read (may be NULL).
+                           Requires kv_int8 = 0. */
 } tilemix_attn_params;
 
 /* Host struct of device pointers for one attention call. */
@@ -135,10 +142,12 @@ typedef struct {
   const void* v;          /* same type and strides as k */
   int64_t q_stride_tok, q_stride_head;    /* elements; multiples of 8; 16-byte aligned base */
   int64_t kv_stride_tok, kv_stride_head;  /* elements; multiples of 8 (fp16) or 16 (int8) */
-  const int8_t* q_q;      /* int8 [N][Hq][d] contiguous, from tilemix_quantize_blockwise(q, blk_q) */
-  const float* q_scale;   /* float32 [Hq][batch][ceil(max_seqlen/blk_q)] */
-  const int8_t* k_q;      /* kv_int8 = 0: int8 [N][Hk][d] contiguous (quantize_blockwise(k, 64)); 1: unused */
-  const float* k_scale;   /* float32 [Hk][batch][T]: per 64-token block of K */
+  const int8_t* q_q;      /* int8 [N][Hq][d] contiguous, from tilemix_quantize_blockwise(q, blk_q);
+                             unused when otf_quant = 1 */
+  const float* q_scale;   /* float32 [Hq][batch][ceil(max_seqlen/blk_q)]; unused when otf_quant = 1 */
+  const int8_t* k_q;      /* kv_int8 = 0: int8 [N][Hk][d] contiguous (quantize_blockwise(k, 64));
+                             unused when kv_int8 = 1 or otf_quant = 1 */
+  const float* k_scale;   /* float32 [Hk][batch][T]: per 64-token block of K; unused when otf_quant = 1 */
   const float* v_scale;   /* kv_int8 = 1: float32 [Hk][batch][T]; 0: unused */
   const int32_t* cu_seqlens;     /* int32 [batch+1] */
   const uint64_t* route_words;   /* uint64 [Hk][batch][T] from tilemix_build_route_mask */
@@ -160,6 +169,7 @@ int32_t tilemix_attn_workspace_size(const tilemix_attn_params* params, size_t* b
  *                  kv_int8 = 1 uses k = k_int8 * k_scale exactly)
  *   R = 1 (INT8):  s_ij = sm_scale * q_scale(i) * k_scale(j) * S32_ij,
  *                  S32 = int8 MFMA with exact int32 accumulation of q_q . k_q
+ *                  (otf_quant = 1: q_q, k_q and their scales are made on chip)
  * Both paths update one online-softmax state per query row (running max, sum
  * and output accumulator in fp32); P.V runs in fp16 with fp32 accumulation
  * (kv_int8 = 1: v = v_int8 * v_scale, the scale folded into P); the output is

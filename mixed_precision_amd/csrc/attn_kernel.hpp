@@ -47,6 +47,15 @@
 //    only where it moved); acc / l is unchanged.  Raw scores are held in
 //    integer-typed registers (INT8 results as int32, FP16 results as their
 //    float bits) so no float transformation ever touches an int32 bit pattern.
+//  * On-the-fly mode (OTF; the pages' second operand preparation, App. C and
+//    App. D): no Q8/K8 in HBM.  The Q block scales and INT8 Q fragments are made
+//    once per item from fp16 Q; every tile's K arrives as fp16, and only an
+//    INT8-routed tile is quantised, cooperatively, into a separate LDS tile.  Each
+//    wave reads back the K chunks its own lds-loads brought in and publishes
+//    their max |k| before the end-of-tile barrier, so the scale costs no barrier
+//    of its own; one LDS-only barrier separates the quantised tile from its use.
+//    Scales and int8 values equal those of the quantise-once kernel bit for bit,
+//    so both modes give the same output.
 //  * With an fp16 V the normaliser l sums the fp16-rounded probabilities that
 //    actually enter P.V (v_dot2_f32_f16), so O is an exact weighted mean of V
 //    rows with slightly perturbed weights and the dominant term's rounding
@@ -76,6 +85,14 @@ TM_DEV f16x4 read_tr16(const char* p) {
   return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
 }
 TM_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
+// Workgroup barrier that waits for this wave's LDS operations only, not for
+// its global loads in flight (which __syncthreads would also drain).
+TM_DEV void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D, int QB, bool KVI8>
 struct Attn {
@@ -147,6 +164,33 @@ struct Attn {
     }
 #pragma unroll
     for (int i = 0; i < NI16; ++i) bload16_lds(rv, o.b16 + i * s16, vl + (wave * NI16 + i) * LV::BLOCK);
+  }
+
+  // --- on-the-fly K quantisation.  Load i of wave w fills LDS block
+  // w*NI16 + i of the stage's K; its lane l holds channels 8 (l % (RB16/16))
+  // .. +7 of row w*NI16 + i + NB (16 l / RB16), at block + 16 l.  A wave can
+  // read back the chunks of its own loads as soon as they have landed.
+  static constexpr int AMAX_OFF = KBYTES + VBYTES;   // the stage's 4 per-wave maxima
+  static TM_DEV void k_partial_amax(char* st, int wave, int lane) {
+    u16x2 mx = {0, 0};
+#pragma unroll
+    for (int i = 0; i < NI16; ++i)
+      mx = absmax_acc(mx, *reinterpret_cast<const u32x4*>(st + (wave * NI16 + i) * L16::BLOCK + lane * 16));
+    const uint32_t am = wave_max_u32(absmax_bits(mx));
+    if (lane == 0) *reinterpret_cast<uint32_t*>(st + AMAX_OFF + wave * 4) = am;
+  }
+  static TM_DEV float k_tile_scale(const char* st) {
+    const u32x4 p = *reinterpret_cast<const u32x4*>(st + AMAX_OFF);
+    return block_scale(max(max(p[0], p[1]), max(p[2], p[3])));
+  }
+  static TM_DEV void quant_k(const char* st, char* k8, float scale, int wave, int lane) {
+    const float rs = __fdiv_rn(1.0f, scale);
+#pragma unroll
+    for (int i = 0; i < NI16; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + (wave * NI16 + i) * L16::BLOCK + lane * 16);
+      const int R = wave * NI16 + i + L16::NB * ((lane * 16) / RB16);
+      *reinterpret_cast<u32x2*>(k8 + L8::row(R) + ((lane * 16) % RB16) / 2) = quant8(v, scale, rs);
+    }
   }
 
   // --- INT8 KV cache: register staging (16 int8 of one row per thread and load)
@@ -328,16 +372,21 @@ struct Attn {
   }
 };
 
-template <int D, int QB, bool KVI8, bool DBG>
+template <int D, int QB, bool KVI8, bool OTF, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_kernel(const AttnArgs a) {
+  static_assert(!(KVI8 && OTF), "on-the-fly quantisation applies to an fp16 K");
   using A = Attn<D, QB, KVI8>;
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
   // two stages (K tile, then V tile) as two LDS objects: with a fixed object
   // per access the compiler can tell the loads into one stage from reads of
   // the other and does not make those reads wait for the loads
-  __shared__ __attribute__((aligned(1024))) char stA[A::KBYTES + A::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char stB[A::KBYTES + A::VBYTES];
+  constexpr int STAGE = A::KBYTES + A::VBYTES + (OTF ? 16 : 0);
+  __shared__ __attribute__((aligned(1024))) char stA[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stB[STAGE];
+  // on-the-fly mode: the current INT8 tile's K, and per-wave Q-block maxima
+  __shared__ __attribute__((aligned(16))) char k8s[OTF ? A::L8::BYTES : 16];
+  __shared__ uint32_t qam[OTF ? 3 * 4 : 1];
 
   const WorkItem item = a.items[blockIdx.x];
   const int b = uniform(item.b);
@@ -364,14 +413,17 @@ void attn_prefill_kernel(const AttnArgs a) {
   auto qb_row = [&](int j) { return qb_rb(j) * 16 + c; };                           // query offset in tile
   auto qb_valid = [&](int j) { return (j < nh) && (m * kTile + qb_row(j) < L); };
   // q-block scale times sm_scale * log2(e): the INT8 score factor is sqs * k_scale
+  // (wave-uniform values, kept in scalar registers)
   float sqs[QB];
+  if (!OTF) {
 #pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    const int blk_start = m * kTile + qb_rb(j) * 16;
-    float sq = 1.0f;
-    if (j < nh && blk_start < L)
-      sq = a.q_scale[((int64_t)qb_head(j) * a.batch + b) * a.nbq + blk_start / a.blk_q];
-    sqs[j] = sq * a.sm_log2;
+    for (int j = 0; j < QB; ++j) {
+      const int blk_start = m * kTile + qb_rb(j) * 16;
+      float sq = 1.0f;
+      if (j < nh && blk_start < L)
+        sq = a.q_scale[((int64_t)qb_head(j) * a.batch + b) * a.nbq + blk_start / a.blk_q];
+      sqs[j] = sgpr_f32(sq * a.sm_log2);
+    }
   }
 
   // ---- Q operands (B = Q^T): fp16 and int8, loaded once
@@ -388,10 +440,27 @@ void attn_prefill_kernel(const AttnArgs a) {
       qf[j][ds] = valid ? *reinterpret_cast<const f16x8*>(qptr + tok * a.q_st + (int64_t)hqj * a.q_sh + ds * 32 +
                                                          gq * 8)
                         : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (!OTF) {
 #pragma unroll
-    for (int ds = 0; ds < NDS8; ++ds)
-      q8[j][ds] = valid ? *reinterpret_cast<const i32x4*>(a.q_q + (tok * a.Hq + hqj) * D + ds * 64 + gq * 16)
-                        : i32x4{0, 0, 0, 0};
+      for (int ds = 0; ds < NDS8; ++ds)
+        q8[j][ds] = valid ? *reinterpret_cast<const i32x4*>(a.q_q + (tok * a.Hq + hqj) * D + ds * 64 + gq * 16)
+                          : i32x4{0, 0, 0, 0};
+    }
+  }
+  // on-the-fly mode: max |q| over the Q block (blk_q rows of the sequence,
+  // all channels) of every head of the chunk, one partial per wave
+  if (OTF) {
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    const int qb0 = (m * kTile / a.blk_q) * a.blk_q;
+    const int qrows = min(a.blk_q, L - qb0);
+    for (int h = 0; h < nh; ++h) {
+      const f16* src = qptr + (int64_t)(seq0 + qb0) * a.q_st + (int64_t)(hk * a.G + h_begin + h) * a.q_sh;
+      u16x2 mx = {0, 0};
+      for (int id = tid; id < qrows * CPR; id += 256)
+        mx = absmax_acc(mx, *reinterpret_cast<const u32x4*>(src + (int64_t)(id / CPR) * a.q_st + (id % CPR) * 8));
+      const uint32_t am = wave_max_u32(absmax_bits(mx));
+      if (lane == 0) qam[h * 4 + wave] = am;
+    }
   }
 
   // ---- sources: this sequence's rows of KV head hk.  Per tile the buffer
@@ -402,7 +471,8 @@ void attn_prefill_kernel(const AttnArgs a) {
   const char* vbase = static_cast<const char*>(a.v) + ((int64_t)seq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
   const uint32_t kv_stride = (uint32_t)(a.kv_st * esz);
   const uint32_t k8_stride = KVI8 ? kv_stride : (uint32_t)(a.Hk * D);
-  const char* k8base = KVI8 ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)seq0 * a.Hk + hk) * D);
+  const char* k8base =
+      (KVI8 || OTF) ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)seq0 * a.Hk + hk) * D);
   // (empty: a zero-length range, the load reads zeros and touches no memory)
   auto tile_rsrc = [&](const char* base, uint32_t stride, int n, bool empty) __attribute__((always_inline)) {
     const int rows = empty ? 0 : max(L - n * kTile, 0);
@@ -416,7 +486,7 @@ void attn_prefill_kernel(const AttnArgs a) {
   // per-tile scales through the scalar cache (a vector load would be counted
   // behind the tile loads in flight, and waiting for it would wait for them)
   typedef const __attribute__((address_space(4))) float cfloat;
-  cfloat* kscale_row = (cfloat*)(a.k_scale + ((int64_t)hk * a.batch + b) * a.T);
+  cfloat* kscale_row = OTF ? nullptr : (cfloat*)(a.k_scale + ((int64_t)hk * a.batch + b) * a.T);
   cfloat* vscale_row = KVI8 ? (cfloat*)(a.v_scale + ((int64_t)hk * a.batch + b) * a.T) : nullptr;
   // Route of tile n = bit floor(n/g) of the word, tracked incrementally:
   // bit 0 of wsh is the current tile's group, `left` counts the tiles the
@@ -449,14 +519,43 @@ void attn_prefill_kernel(const AttnArgs a) {
   // ---- prologue: tile 0 into stage 0
   {
     typename A::Stage st;
-    fetch(0, (int)(wsh & 1), st, stA, false);
+    fetch(0, OTF ? 0 : (int)(wsh & 1), st, stA, false);
     if (KVI8) {
       wait_vmem();
       A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES);
     }
   }
   wait_vmem();
+  if (OTF && (wsh & 1)) A::k_partial_amax(stA, wave, lane);
   __syncthreads();
+
+  // on-the-fly mode: Q block scales and the INT8 Q operands (channels
+  // 64 ds + 16 gq .. +15 of the lane's query row)
+  if (OTF) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      float sq = 1.0f;
+      if (j < nh) {
+        const int hj = (wave * nh + j) >> 2;
+        sq = uniform(block_scale(max(max(qam[hj * 4], qam[hj * 4 + 1]), max(qam[hj * 4 + 2], qam[hj * 4 + 3]))));
+      }
+      sqs[j] = sgpr_f32(sq * a.sm_log2);
+      const float rs = __fdiv_rn(1.0f, sq);
+      const int64_t tok = (int64_t)seq0 + m * kTile + qb_row(j);
+      const bool valid = qb_valid(j);
+      const f16* src = qptr + tok * a.q_st + (int64_t)qb_head(j) * a.q_sh + gq * 16;
+#pragma unroll
+      for (int ds = 0; ds < NDS8; ++ds) {
+        if (valid) {
+          const u32x2 lo = quant8(*reinterpret_cast<const u32x4*>(src + ds * 64), sq, rs);
+          const u32x2 hi = quant8(*reinterpret_cast<const u32x4*>(src + ds * 64 + 8), sq, rs);
+          q8[j][ds] = __builtin_bit_cast(i32x4, u32x4{lo.x, lo.y, hi.x, hi.y});
+        } else {
+          q8[j][ds] = i32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  }
 
   // Tile n: tile n+1's loads are issued first (into the other stage, last
   // read in step n-1; after the last tile they read nothing), then tile n is
@@ -471,8 +570,19 @@ void attn_prefill_kernel(const AttnArgs a) {
     const char* kl = cur;
     const char* vl = cur + A::KBYTES;
     typename A::Stage st;
-    fetch(n + 1, rnext, st, next, last);
-    const float ksc = kscale_row[n];
+    fetch(n + 1, OTF ? 0 : rnext, st, next, last);
+    // on-the-fly mode, INT8 tile: quantise the stage's fp16 K into k8s
+    float ksc;
+    if (OTF) {
+      ksc = 1.0f;
+      if (rc) {
+        ksc = uniform(A::k_tile_scale(cur));
+        A::quant_k(cur, k8s, ksc, wave, lane);
+        lds_barrier();
+      }
+    } else {
+      ksc = kscale_row[n];
+    }
     // score factors, kept > 0 so a (caller-supplied) zero scale cannot turn a
     // masked -inf into NaN
     float cj[QB];
@@ -505,7 +615,7 @@ void attn_prefill_kernel(const AttnArgs a) {
       if (rc == 0) {
         A::qk16(kl, h, qf, S, c, gq);
       } else {
-        A::qk8(kl, h, q8, S, c, gq);
+        A::qk8(OTF ? k8s : kl, h, q8, S, c, gq);
         if (DBG) {
 #pragma unroll
           for (int j = 0; j < QB; ++j) {
@@ -537,6 +647,8 @@ void attn_prefill_kernel(const AttnArgs a) {
       A::stage_store(st, rnext, tid, next, next + A::KBYTES);
     }
     wait_vmem();
+    // on-the-fly mode: this wave's max |k| of an INT8 next tile
+    if (OTF && rnext && !last) A::k_partial_amax(next, wave, lane);
     __syncthreads();
     if (--left == 0) {
       left = g;
@@ -575,9 +687,9 @@ void attn_prefill_kernel(const AttnArgs a) {
   }
 }
 
-template <int D, int QB, bool KVI8, bool DBG>
+template <int D, int QB, bool KVI8, bool OTF, bool DBG>
 hipError_t launch_attn_inst(const AttnArgs& a, int64_t nslots, hipStream_t s) {
-  hipLaunchKernelGGL((attn_prefill_kernel<D, QB, KVI8, DBG>), dim3((unsigned)nslots), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_prefill_kernel<D, QB, KVI8, OTF, DBG>), dim3((unsigned)nslots), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

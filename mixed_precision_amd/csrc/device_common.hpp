@@ -24,9 +24,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 TM_DEV int lane_id() { return __lane_id(); }
 
+// Value of the first active lane (a wave-uniform value), bit for bit: the
+// builtin is int-typed, so other 32-bit types go through a bit cast, never a
+// numeric conversion.
 template <typename T>
 TM_DEV T uniform(T x) {
-  return __builtin_amdgcn_readfirstlane(x);
+  static_assert(sizeof(T) == 4, "uniform() takes a 32-bit value");
+  return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+// A wave-uniform float pinned to a scalar register.  (The compiler drops a
+// readfirstlane of a value it already knows to be uniform and may then keep
+// the value in a vector register; long-lived per-wave constants belong in SGPRs.)
+// The compiler's hazard recognizer does not look inside an asm block, so the
+// block carries its own wait states: a VALU write of x just before (1 needed),
+// and VALU (2) or VMEM (5) reads of the result just after.
+TM_DEV float sgpr_f32(float x) {
+  float r;
+  asm volatile("s_nop 1\n\tv_readfirstlane_b32 %0, %1\n\ts_nop 4" : "=s"(r) : "v"(x));
+  return r;
 }
 TM_DEV uint64_t uniform64(uint64_t x) {
   uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
@@ -34,24 +49,61 @@ TM_DEV uint64_t uniform64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-TM_DEV float wave_max(float v) {
+TM_DEV uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
   return v;
 }
 
-// XOR swizzle of 16-byte chunks inside an LDS row so that the 16 lanes of an
-// MFMA operand read (16 consecutive rows, same logical chunk) hit distinct banks.
-// row_bytes in {64, 128, 256}.
-template <int ROW_BYTES>
-TM_DEV int swz_chunk(int row, int chunk) {
-  constexpr int cpr = ROW_BYTES / 16;      // chunks per row
-  constexpr int rpp = 256 / ROW_BYTES;     // rows per 256-byte bank period
-  return chunk ^ ((row / rpp) % cpr);
+// ---- blockwise symmetric INT8 quantisation, bit-exact with the definition
+//   a = max|x|, scale = fl32(a/127), q = clamp(rint_half_even(fl32(x/scale)), +-127),
+//   an all-zero block taking scale 1 and q = 0.
+//  * a is taken on the fp16 bit patterns (|x| bits order like the values), two
+//    per packed u16 max;
+//  * scale and r = fl32(1/scale) are correctly rounded divisions, once per
+//    block; per element q0 = fl32(x r), e = x - q0 scale (one fma, exact) and
+//    q1 = fl32(q0 + e r) is the correctly rounded quotient fl32(x/scale) (the
+//    correction step of Markstein's division; checked for every finite fp16 x
+//    with |x| <= a against every scale a fp16 block can produce: the only
+//    difference is the sign of a zero quotient, which does not reach the int8);
+//  * adding 1.5 * 2^23 rounds q1 to an integer with ties to even, and the low
+//    byte of the sum's bit pattern is that integer in two's complement;
+//  * |q1| <= 127 (1 + 2^-23) because scale >= a/127 (1 - 2^-24), so the clamp
+//    never binds and is not applied.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// running max of |x| over 8 fp16 (one 16-byte chunk), as two packed u16 lanes
+TM_DEV u16x2 absmax_acc(u16x2 mx, const u32x4 v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, v[e] & 0x7FFF7FFFu));
+  return mx;
+}
+TM_DEV uint32_t absmax_bits(u16x2 mx) { return max((uint32_t)mx[0], (uint32_t)mx[1]); }
+
+// block scale from the fp16 bits of a = max|x|
+TM_DEV float block_scale(uint32_t abits) {
+  const float amax = (float)__builtin_bit_cast(f16, (unsigned short)abits);
+  return (abits == 0) ? 1.0f : __fdiv_rn(amax, 127.0f);
 }
 
-// V^T rows hold 64 keys = 16 units of 8 bytes; swizzle of the unit index.
-TM_DEV int swz_vt(int d, int unit) { return unit ^ (d & 14); }
+// 8 fp16 -> 8 int8 (two dwords, element 0 in the lowest byte); rs = fl32(1/scale)
+TM_DEV u32x2 quant8(const u32x4 v, float scale, float rs) {
+  const f16x8 hv = __builtin_bit_cast(f16x8, v);
+  uint32_t byte[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xf = (float)hv[e];
+    const float q0 = xf * rs;
+    const float er = __builtin_fmaf(-q0, scale, xf);
+    const float q1 = __builtin_fmaf(er, rs, q0);
+    byte[e] = __builtin_bit_cast(uint32_t, q1 + 12582912.0f);
+  }
+  const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(byte[3], byte[2], 0x0c0c0400u),
+                                            __builtin_amdgcn_perm(byte[1], byte[0], 0x0c0c0400u), 0x05040100u);
+  const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(byte[7], byte[6], 0x0c0c0400u),
+                                            __builtin_amdgcn_perm(byte[5], byte[4], 0x0c0c0400u), 0x05040100u);
+  return u32x2{lo, hi};
+}
 
 // Four int8 (one dword) -> four fp16 (two dwords), exact: bias the bytes to
 // unsigned, splice them under the fp16 exponent of 1024 (bits 0x64uu encode
@@ -72,14 +124,6 @@ TM_DEV void i8x16_to_f16x16(const u32x4 w, u32x4& c0, u32x4& c1) {
   const u32x2 c = i8x4_to_f16x4(w.z), d = i8x4_to_f16x4(w.w);
   c0 = u32x4{a.x, a.y, b.x, b.y};
   c1 = u32x4{c.x, c.y, d.x, d.y};
-}
-
-// Transpose a 4-key x 8-channel fp16 block: rows r0..r3 hold channels 0..7 of
-// keys 0..3; column x (channel x of keys 0..3, 8 bytes) is returned per x.
-TM_DEV u32x2 vt_column(const u32x4& r0, const u32x4& r1, const u32x4& r2, const u32x4& r3, int x) {
-  const int w = x >> 1;
-  const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
-  return u32x2{__builtin_amdgcn_perm(r1[w], r0[w], sel), __builtin_amdgcn_perm(r3[w], r2[w], sel)};
 }
 
 }  // namespace tilemix

@@ -75,6 +75,9 @@ int32_t validate_attn_params(const tilemix_attn_params* p) {
   if (p->causal != 1) return fail(TILEMIX_ERR_UNSUPPORTED, "causal = %d: only causal prefill is implemented", p->causal);
   if (p->kv_int8 != 0 && p->kv_int8 != 1) return fail(TILEMIX_ERR_INVALID_ARG, "kv_int8 must be 0 or 1");
   if (p->out_fp32 != 0 && p->out_fp32 != 1) return fail(TILEMIX_ERR_INVALID_ARG, "out_fp32 must be 0 or 1");
+  if (p->otf_quant != 0 && p->otf_quant != 1) return fail(TILEMIX_ERR_INVALID_ARG, "otf_quant must be 0 or 1");
+  if (p->otf_quant && p->kv_int8)
+    return fail(TILEMIX_ERR_UNSUPPORTED, "otf_quant = 1 quantises an fp16 K: it cannot be combined with kv_int8 = 1");
   if (!(p->sm_scale > 0.0f) || !std::isfinite(p->sm_scale))
     return fail(TILEMIX_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   int32_t st = check_groups(p->max_seqlen, p->g);
@@ -107,16 +110,18 @@ Derived derive(const tilemix_attn_params* p) {
 int32_t validate_tensors(const tilemix_attn_params* p, const tilemix_attn_tensors* t) {
   if (!t) return fail(TILEMIX_ERR_INVALID_ARG, "tensors is NULL");
   if (!t->q || !t->k || !t->v) return fail(TILEMIX_ERR_INVALID_ARG, "q, k and v must be non-NULL");
-  if (!t->q_q || !t->q_scale) return fail(TILEMIX_ERR_INVALID_ARG, "q_q and q_scale must be non-NULL");
-  if (!t->k_scale) return fail(TILEMIX_ERR_INVALID_ARG, "k_scale must be non-NULL");
-  if (!p->kv_int8 && !t->k_q) return fail(TILEMIX_ERR_INVALID_ARG, "k_q must be non-NULL when kv_int8 = 0");
+  const bool otf = p->otf_quant != 0;
+  if (!otf && (!t->q_q || !t->q_scale)) return fail(TILEMIX_ERR_INVALID_ARG, "q_q and q_scale must be non-NULL");
+  if (!otf && !t->k_scale) return fail(TILEMIX_ERR_INVALID_ARG, "k_scale must be non-NULL");
+  if (!otf && !p->kv_int8 && !t->k_q)
+    return fail(TILEMIX_ERR_INVALID_ARG, "k_q must be non-NULL when kv_int8 = 0");
   if (p->kv_int8 && !t->v_scale) return fail(TILEMIX_ERR_INVALID_ARG, "v_scale must be non-NULL when kv_int8 = 1");
   if (!t->cu_seqlens || !t->route_words || !t->out)
     return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens, route_words and out must be non-NULL");
-  if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16) || !aligned(t->q_q, 16) ||
-      (t->k_q && !aligned(t->k_q, 16)) || !aligned(t->out, 16))
+  if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16) || (!otf && !aligned(t->q_q, 16)) ||
+      (!otf && t->k_q && !aligned(t->k_q, 16)) || !aligned(t->out, 16))
     return fail(TILEMIX_ERR_INVALID_ARG, "q, k, v, q_q, k_q and out must be 16-byte aligned");
-  if (!aligned(t->route_words, 8) || !aligned(t->q_scale, 4) || !aligned(t->k_scale, 4) ||
+  if (!aligned(t->route_words, 8) || (!otf && (!aligned(t->q_scale, 4) || !aligned(t->k_scale, 4))) ||
       !aligned(t->cu_seqlens, 4) || (t->v_scale && !aligned(t->v_scale, 4)))
     return fail(TILEMIX_ERR_INVALID_ARG, "misaligned scale, cu_seqlens or route_words pointer");
   const int64_t kv_mult = p->kv_int8 ? 16 : 8;
@@ -216,6 +221,13 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
   a.sm_log2 = (float)((double)p->sm_scale * 1.4426950408889634);
   a.out_fp32 = p->out_fp32;
   a.kv_int8 = p->kv_int8;
+  a.otf = p->otf_quant;
+  if (a.otf) {   // not read in this mode
+    a.q_q = nullptr;
+    a.q_scale = nullptr;
+    a.k_q = nullptr;
+    a.k_scale = nullptr;
+  }
   a.dbg_seq = -1;
   if (dbg) {
     const int64_t tiles = (int64_t)p->batch * p->num_q_heads * d.T * d.T;
@@ -270,10 +282,16 @@ hipError_t launch_attn_d64_kv0(const AttnArgs&, int64_t, bool, hipStream_t);
 hipError_t launch_attn_d64_kv1(const AttnArgs&, int64_t, bool, hipStream_t);
 hipError_t launch_attn_d128_kv0(const AttnArgs&, int64_t, bool, hipStream_t);
 hipError_t launch_attn_d128_kv1(const AttnArgs&, int64_t, bool, hipStream_t);
+hipError_t launch_attn_d64_otf(const AttnArgs&, int64_t, bool, hipStream_t);
+hipError_t launch_attn_d128_otf(const AttnArgs&, int64_t, bool, hipStream_t);
 
 hipError_t launch_attn(const AttnArgs& a, int64_t nslots, bool debug, hipStream_t s) {
-  if (a.D == 64) return a.kv_int8 ? launch_attn_d64_kv1(a, nslots, debug, s) : launch_attn_d64_kv0(a, nslots, debug, s);
-  return a.kv_int8 ? launch_attn_d128_kv1(a, nslots, debug, s) : launch_attn_d128_kv0(a, nslots, debug, s);
+  if (a.D == 64) {
+    if (a.kv_int8) return launch_attn_d64_kv1(a, nslots, debug, s);
+    return a.otf ? launch_attn_d64_otf(a, nslots, debug, s) : launch_attn_d64_kv0(a, nslots, debug, s);
+  }
+  if (a.kv_int8) return launch_attn_d128_kv1(a, nslots, debug, s);
+  return a.otf ? launch_attn_d128_otf(a, nslots, debug, s) : launch_attn_d128_kv0(a, nslots, debug, s);
 }
 
 }  // namespace tilemix

@@ -40,7 +40,7 @@ class AttnParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_seqlen", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("g", ctypes.c_int32),
                 ("blk_q", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("kv_int8", ctypes.c_int32), ("out_fp32", ctypes.c_int32)]
+                ("kv_int8", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("otf_quant", ctypes.c_int32)]
 
 
 class AttnTensors(ctypes.Structure):
@@ -188,10 +188,12 @@ class AttnProblem:
     sm_scale: float
     kv_int8: bool = False
     out_fp32: bool = False
+    otf_quant: bool = False   # Q/K INT8 operands made inside the kernel (q_q, q_scale, k_q, k_scale unused)
 
     def params(self) -> AttnParams:
         return AttnParams(self.batch, self.max_seqlen, self.num_q_heads, self.num_kv_heads, self.head_dim, self.g,
-                          self.blk_q, float(self.sm_scale), 1, int(self.kv_int8), int(self.out_fp32))
+                          self.blk_q, float(self.sm_scale), 1, int(self.kv_int8), int(self.out_fp32),
+                          int(self.otf_quant))
 
 
 def tilemix_attn_workspace_size(problem: AttnProblem) -> int:
@@ -208,9 +210,10 @@ def _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_wor
         if t.shape[dim] > 1:
             return t.stride(dim)
         return t.shape[2] * (t.shape[1] if dim == 0 else 1)
+    def p(t):
+        return None if t is None else t.data_ptr()
     return AttnTensors(q.data_ptr(), k.data_ptr(), v.data_ptr(), st(q, 0), st(q, 1), st(k, 0), st(k, 1),
-                       q_q.data_ptr(), q_scale.data_ptr(), None if k_q is None else k_q.data_ptr(),
-                       k_scale.data_ptr(), None if v_scale is None else v_scale.data_ptr(), cu_seqlens.data_ptr(),
+                       p(q_q), p(q_scale), p(k_q), p(k_scale), p(v_scale), cu_seqlens.data_ptr(),
                        route_words.data_ptr(), out.data_ptr())
 
 
@@ -250,11 +253,14 @@ class AttnPlan:
         return out
 
 
-def tilemix_attn_prefill(q, k, v, *, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, max_seqlen: int,
-                         g: int, blk_q: int = 64, sm_scale: Optional[float] = None, kv_int8: bool = False,
-                         v_scale=None, out_fp32: bool = False, out=None, plan: Optional[AttnPlan] = None,
-                         stream=None) -> torch.Tensor:
-    """Fused routed causal prefill attention; returns out [N][Hq][d] (fp16, or fp32 if out_fp32)."""
+def tilemix_attn_prefill(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g: int, q_q=None, q_scale=None,
+                         k_q=None, k_scale=None, blk_q: int = 64, sm_scale: Optional[float] = None,
+                         kv_int8: bool = False, v_scale=None, out_fp32: bool = False, otf_quant: bool = False,
+                         out=None, plan: Optional[AttnPlan] = None, stream=None) -> torch.Tensor:
+    """Fused routed causal prefill attention; returns out [N][Hq][d] (fp16, or fp32 if out_fp32).
+
+    otf_quant=False takes the quantise-once operands q_q, q_scale, k_q, k_scale (k_q unused with kv_int8);
+    otf_quant=True makes them inside the kernel and ignores those arguments."""
     N, Hq, d = q.shape
     Hk = k.shape[1]
     B = cu_seqlens.numel() - 1
@@ -262,16 +268,17 @@ def tilemix_attn_prefill(q, k, v, *, q_q, q_scale, k_q, k_scale, cu_seqlens, rou
         sm_scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     if plan is None:
         plan = AttnPlan(AttnProblem(B, int(max_seqlen), Hq, Hk, d, int(g), int(blk_q), float(sm_scale),
-                                    bool(kv_int8), bool(out_fp32)), device=q.device)
+                                    bool(kv_int8), bool(out_fp32), bool(otf_quant)), device=q.device)
     if out is None:
         out = torch.empty((N, Hq, d), dtype=torch.float32 if out_fp32 else torch.float16, device=q.device)
     return plan.run(q, k, v, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, out, v_scale=v_scale,
                     stream=stream)
 
 
-def tilemix_attn_prefill_debug(q, k, v, *, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, max_seqlen: int,
-                               g: int, blk_q: int = 64, sm_scale: Optional[float] = None, kv_int8: bool = False,
-                               v_scale=None, out_fp32: bool = True, seq: int = 0, q_head: int = 0,
+def tilemix_attn_prefill_debug(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g: int, q_q=None,
+                               q_scale=None, k_q=None, k_scale=None, blk_q: int = 64,
+                               sm_scale: Optional[float] = None, kv_int8: bool = False, v_scale=None,
+                               out_fp32: bool = True, otf_quant: bool = False, seq: int = 0, q_head: int = 0,
                                m_begin: int = 0, m_end: Optional[int] = None, stream=None):
     """As tilemix_attn_prefill, plus (s32_tiles, visit_count, route_used) debug products."""
     N, Hq, d = q.shape
@@ -283,7 +290,7 @@ def tilemix_attn_prefill_debug(q, k, v, *, q_q, q_scale, k_q, k_scale, cu_seqlen
     if sm_scale is None:
         sm_scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     plan = AttnPlan(AttnProblem(B, int(max_seqlen), Hq, Hk, d, int(g), int(blk_q), float(sm_scale), bool(kv_int8),
-                                bool(out_fp32)), device=q.device)
+                                bool(out_fp32), bool(otf_quant)), device=q.device)
     out = torch.empty((N, Hq, d), dtype=torch.float32 if out_fp32 else torch.float16, device=q.device)
     s32 = torch.empty((m_end - m_begin, T, TILE, TILE), dtype=torch.int32, device=q.device)
     visits = torch.empty((B, Hq, T, T), dtype=torch.int32, device=q.device)

@@ -33,7 +33,11 @@ def prepare(w: Workload, dev=DEV, t=None):
     return t
 
 
-def attn(w: Workload, t, out_fp32=True, plan=None, out=None):
+def attn(w: Workload, t, out_fp32=True, plan=None, out=None, otf=False):
+    if otf:   # on-the-fly quantisation: only fp16 q, k, v, the route words and cu_seqlens
+        return tm.tilemix_attn_prefill(t["q"], t["k"], t["v"], cu_seqlens=t["cu"], route_words=t["words"],
+                                       max_seqlen=w.max_seqlen, g=w.g, blk_q=w.blk_q, sm_scale=w.sm_scale,
+                                       out_fp32=out_fp32, otf_quant=True, plan=plan, out=out)
     if w.kv_int8:
         return tm.tilemix_attn_prefill(t["q"], t["k8"], t["v8"], q_q=t["q_q"], q_scale=t["q_s"], k_q=None,
                                        k_scale=t["k_s"], v_scale=t["v_s"], kv_int8=True, cu_seqlens=t["cu"],
@@ -45,10 +49,13 @@ def attn(w: Workload, t, out_fp32=True, plan=None, out=None):
                                    out_fp32=out_fp32, plan=plan, out=out)
 
 
-def attn_debug(w: Workload, t, seq=0, q_head=0, m_begin=0, m_end=None):
+def attn_debug(w: Workload, t, seq=0, q_head=0, m_begin=0, m_end=None, otf=False):
     kw = dict(q_q=t["q_q"], q_scale=t["q_s"], k_scale=t["k_s"], cu_seqlens=t["cu"], route_words=t["words"],
               max_seqlen=w.max_seqlen, g=w.g, blk_q=w.blk_q, sm_scale=w.sm_scale, seq=seq, q_head=q_head,
               m_begin=m_begin, m_end=m_end)
+    if otf:
+        kw.update(q_q=None, q_scale=None, k_scale=None, otf_quant=True)
+        return tm.tilemix_attn_prefill_debug(t["q"], t["k"], t["v"], **kw)
     if w.kv_int8:
         return tm.tilemix_attn_prefill_debug(t["q"], t["k8"], t["v8"], k_q=None, v_scale=t["v_s"], kv_int8=True, **kw)
     return tm.tilemix_attn_prefill_debug(t["q"], t["k"], t["v"], k_q=t["k_q"], **kw)

@@ -106,6 +106,25 @@ def test_null_pointer_and_workspace_errors(tm):
     assert lib.tilemix_attn_run(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 1
 
 
+def test_on_the_fly_mode_validation(tm):
+    """otf_quant: 0 or 1, not with an INT8 KV cache; in that mode the quantise-once
+    operands may be NULL (the call then fails only on the missing workspace)."""
+    lib = tm.lib()
+    a = 1 << 20
+    t = tm.AttnTensors(a, a, a, 24 * 128, 128, 8 * 128, 128, None, None, None, None, None, a, a, a)
+    p = _params(tm, otf_quant=True).params()
+    assert lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 4
+    assert lib.tilemix_attn_run(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 4
+    p0 = _params(tm).params()
+    assert lib.tilemix_attn_prefill(ctypes.byref(p0), ctypes.byref(t), None, 0, None) == 1
+    assert "q_q" in tm.last_error()
+    p.otf_quant = 2
+    assert lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 1
+    with pytest.raises(tm.TilemixError) as e:
+        tm.tilemix_attn_workspace_size(_params(tm, otf_quant=True, kv_int8=True))
+    assert e.value.status == 2 and "kv_int8" in str(e.value)
+
+
 def test_quantize_and_route_validation(tm):
     lib = tm.lib()
     a = ctypes.c_void_p(1 << 20)

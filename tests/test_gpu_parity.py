@@ -224,6 +224,78 @@ def test_attn_debug_bitexact(gp, case):
     assert ma <= MAX_ABS and rf <= REL_FRO
 
 
+OTF_SMALL = [c for c in SMALL if not c[8]]
+
+
+@pytest.mark.parametrize("case", OTF_SMALL, ids=[c[0] for c in OTF_SMALL])
+def test_attn_on_the_fly_equals_quantize_once(gp, case):
+    """On-the-fly quantisation (Q/K INT8 fragments and block scales made inside
+    the kernel) follows the same blockwise definition as the quantiser, so its
+    output equals the quantise-once output bit for bit (fp32 and fp16 outputs),
+    and therefore meets the oracle bar too."""
+    import torch
+    name, lengths, hq, hk, d, g, route, p, kv8, blk_q, outl = case
+    _announce(f"attn on-the-fly {name}")
+    extra = dict(q_outlier_scale=1.0, k_outlier_scale=10.0) if outl == "mild" else {}
+    w = make_workload(400 + SMALL.index(case), lengths=lengths, num_q_heads=hq, num_kv_heads=hk, head_dim=d, g=g,
+                      route=route, p=p, kv_int8=kv8, blk_q=blk_q, outliers=bool(outl), **extra)
+    t = gp.prepare(w)
+    once32 = gp.attn(w, t, out_fp32=True)
+    otf32 = gp.attn(w, t, out_fp32=True, otf=True)
+    once16 = gp.attn(w, t, out_fp32=False)
+    otf16 = gp.attn(w, t, out_fp32=False, otf=True)
+    torch.cuda.synchronize()
+    assert torch.equal(otf32, once32)
+    assert torch.equal(otf16, once16)
+    ma, rf = gp.errors(otf32.cpu().numpy(), orc.attn_prefill(oracle_inputs(w)))
+    print(f"  max_abs={ma:.3e} rel_fro={rf:.3e}")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+@pytest.mark.parametrize("case", ["tiny", "gqa3_varlen_blkq128"])
+def test_attn_on_the_fly_debug_bitexact(gp, case):
+    """On-the-fly mode: INT32 score tiles bit-exact against the oracle's (so the
+    on-chip Q/K quantisation and block layout are exact), visits and routes too."""
+    import torch
+    _announce(f"attn on-the-fly debug {case}")
+    if case == "tiny":
+        w = config(1)
+        seq, head = 0, 0
+    else:
+        w = make_workload(452, lengths=[130, 300, 64], num_q_heads=6, num_kv_heads=2, head_dim=128, g=2,
+                          p=0.6, outliers=True, blk_q=128)
+        seq, head = 1, 4
+    t = gp.prepare(w)
+    out, s32, visits, used = gp.attn_debug(w, t, seq=seq, q_head=head, otf=True)
+    torch.cuda.synchronize()
+    inp = oracle_inputs(w)
+    assert np.array_equal(s32.cpu().numpy(), orc.s32_tiles(inp, seq, head, 0, w.T))
+    vis = orc.visit_matrix(w.cu_seqlens, w.max_seqlen, w.num_q_heads)
+    assert np.array_equal(visits.cpu().numpy().astype(np.uint32), vis)
+    assert np.array_equal(used.cpu().numpy(), orc.route_used(inp))
+    ma, rf = gp.errors(out.cpu().numpy(), orc.attn_prefill(inp))
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+def test_attn_on_the_fly_zero_blocks(gp):
+    """On-the-fly mode with an all-zero Q block and an all-zero K tile (scale 1,
+    int8 zeros by definition): same output as quantise-once and the oracle."""
+    import torch
+    _announce("attn on-the-fly zero blocks")
+    w = make_workload(471, lengths=[200, 150], num_q_heads=3, num_kv_heads=1, head_dim=128, g=1, route="ones",
+                      p=1.0, outliers=True)
+    s1 = int(w.cu_seqlens[1])
+    w.q[64:128, 1, :] = 0
+    w.k[s1 + 64:s1 + 128, 0, :] = 0
+    t = gp.prepare(w)
+    once = gp.attn(w, t)
+    otf = gp.attn(w, t, otf=True)
+    torch.cuda.synchronize()
+    assert torch.equal(otf, once)
+    ma, rf = gp.errors(otf.cpu().numpy(), orc.attn_prefill(oracle_inputs(w)))
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
 def test_attn_zero_scale_blocks(gp):
     """A caller may pass scale 0 for an all-zero INT8 block (the library's own
     quantiser writes 1.0 there).  The INT32 scores of such a block are 0 either
@@ -295,10 +367,46 @@ def test_standard_config_scaled_full(gp, cfg):
     w = config(cfg, scale_down=1 if cfg == 1 else (16 if cfg == 5 else 8))
     t = gp.prepare(w)
     out = gp.attn(w, t)
+    otf = None if w.kv_int8 else gp.attn(w, t, otf=True)
     torch.cuda.synchronize()
     ref = orc.attn_prefill(oracle_inputs(w))
     ma, rf = gp.errors(out.cpu().numpy(), ref)
     print(f"  {w.name}: max_abs={ma:.3e} rel_fro={rf:.3e}")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+    if otf is not None:   # on-the-fly quantisation: the same bits
+        assert torch.equal(otf, out)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.25, 0.75, 1.0])
+def test_long_context_coverage_sweep_scaled(gp, p):
+    """The long-context workload's INT8 coverage sweep (0/25/50/75/100 % of the
+    tile groups; 50 % is the standard case above) at 1/16 of its length."""
+    import torch
+    _announce(f"config 5 scaled, coverage {p}")
+    w = config(5, p=p, scale_down=16)
+    t = gp.prepare(w)
+    out = gp.attn(w, t)
+    torch.cuda.synchronize()
+    ref = orc.attn_prefill(oracle_inputs(w))
+    ma, rf = gp.errors(out.cpu().numpy(), ref)
+    print(f"  {w.name}: max_abs={ma:.3e} rel_fro={rf:.3e}")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+def test_3b_workload_blkq128_scaled(gp):
+    """The 3B-shaped layer with Q quantised in blocks of 128 tokens (the pages'
+    BLKQ; the default is 64), at 1/8 of its length, compared in full."""
+    import torch
+    _announce("config 2 scaled, blk_q 128")
+    w = config(2, scale_down=8)
+    w.blk_q = 128
+    t = gp.prepare(w)
+    out = gp.attn(w, t)
+    torch.cuda.synchronize()
+    inp = oracle_inputs(w)
+    assert np.array_equal(t["q_s"].cpu().numpy(), inp.q_scale)
+    ma, rf = gp.errors(out.cpu().numpy(), orc.attn_prefill(inp))
+    print(f"  max_abs={ma:.3e} rel_fro={rf:.3e}")
     assert ma <= MAX_ABS and rf <= REL_FRO
 
 
