@@ -120,6 +120,55 @@ def cpu_baseline(w, budget_s=15.0):
                       f"legal-tile work"}
 
 
+def deviation_sweep(args, w, plan, q, k, v, cu, q_q, q_s, k_q, k_s, v_q, v_s, words, stream):
+    """Coverage -> deviation: the same inputs routed at each INT8 coverage p; MaxDiff and MeanDiff
+    (largest and mean absolute elementwise difference, all tokens/heads/channels) of the fp32 output
+    against the 0 % output, which takes the FP16 path on every tile."""
+    import torch
+    from mixed_precision_amd import tilemix as tm
+    from workloads import route_bernoulli_groups
+    if args.config == 3:
+        raise SystemExit("--deviation-sweep needs a Bernoulli-routed workload (configs 1, 2, 4, 5)")
+    dev = q.device
+    ps = [float(x) for x in args.deviation_sweep.split(",")]
+    if 0.0 not in ps:
+        ps = [0.0] + ps
+    N, Hq, d = w.q.shape
+    plan32 = tm.AttnPlan(tm.AttnProblem(w.batch, w.max_seqlen, Hq, w.num_kv_heads, d, w.g, w.blk_q, w.sm_scale,
+                                        w.kv_int8, True), dev)
+    tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
+    if w.kv_int8:
+        tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
+        tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
+    else:
+        tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
+    plan32.schedule(cu, stream=stream)
+    ref = None
+    outs = {}
+    for p in sorted(set(ps)):
+        tr = torch.from_numpy(route_bernoulli_groups(w.cfg_id, w.num_kv_heads, [int(x) for x in w.lengths], w.T,
+                                                     w.g, p)).to(dev)
+        tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
+        work = work_model(w, words.cpu().numpy().view(np.uint64))
+        out = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if w.kv_int8:
+            plan32.run_planned(q, k_q, v_q, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream)
+        else:
+            plan32.run_planned(q, k, v, q_q, q_s, k_q, k_s, cu, words, out, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = out
+        diff = (out - ref).abs()
+        res = {"deviation_sweep": w.name, "p": p, "int8_pair_fraction": work["pairs_int8"] / work["pairs"],
+               "max_diff": float(diff.max()), "mean_diff": float(diff.double().mean()),
+               "reference": "same inputs at 0 % INT8 (all tiles FP16)", "attn_ms_fp32_out": e0.elapsed_time(e1)}
+        del diff
+        print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +179,9 @@ def main():
     ap.add_argument("--otf", action="store_true",
                     help="on-the-fly quantisation: Q/K INT8 operands made inside the attention kernel "
                          "(no quantiser calls in the step)")
+    ap.add_argument("--deviation-sweep", type=str, default=None, metavar="P,P,...",
+                    help="instead of the bench line: MaxDiff / MeanDiff of the routed output against the "
+                         "0 %% INT8 output at each INT8 coverage (Bernoulli-routed workloads), one JSON line each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -177,6 +229,9 @@ def main():
     words = torch.empty((Hk, B, T), dtype=torch.int64, device=dev)
     out = torch.empty((N, Hq, d), dtype=torch.float16, device=dev)
     stream = torch.cuda.current_stream()
+    if args.deviation_sweep:
+        deviation_sweep(args, w, plan, q, k, v, cu, q_q, q_s, k_q, k_s, v_q, v_s, words, stream)
+        return
     tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
     work = work_model(w, words.cpu().numpy().view(np.uint64))
 

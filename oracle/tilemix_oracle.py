@@ -454,6 +454,25 @@ def attn_brute_force(inp: AttnInputs, b: int, hq: int) -> List[List[float]]:
 
 
 # ---------------------------------------------------------------------------
+# Numerical deviation [PL §5 Numerical Behavior], [PL App. G, G.1, G.2]
+# ---------------------------------------------------------------------------
+
+def output_deviation(o: np.ndarray, o_ref: np.ndarray) -> Tuple[float, float]:
+    """(MaxDiff, MeanDiff) of an attention output against a reference output.
+
+    The pages measure routed outputs against a fixed FP16 reference with the
+    maximum and the mean elementwise difference.  Reading taken: both are
+    absolute differences over every output element (all tokens, heads and
+    channels), computed in float64."""
+    if o.shape != o_ref.shape:
+        raise ValueError("shape mismatch")
+    diff = np.abs(o.astype(np.float64) - o_ref.astype(np.float64))
+    if diff.size == 0:
+        return 0.0, 0.0
+    return float(diff.max()), float(diff.mean())
+
+
+# ---------------------------------------------------------------------------
 # Resident-footprint calculator [PL App. D]
 # ---------------------------------------------------------------------------
 

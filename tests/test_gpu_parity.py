@@ -410,6 +410,36 @@ def test_3b_workload_blkq128_scaled(gp):
     assert ma <= MAX_ABS and rf <= REL_FRO
 
 
+def test_deviation_sweep_matches_oracle(gp):
+    """Coverage -> deviation ([PL §5 Numerical Behavior], [PL App. G]) on a
+    long-context-shaped head group: MaxDiff / MeanDiff of the routed output
+    against the 0 % output agree with the oracle's; 0 % is exactly zero; the
+    mean deviation at 100 % exceeds that at 10 %."""
+    import torch
+    _announce("deviation sweep")
+    ps = [0.0, 0.1, 0.5, 1.0]
+    got, ref = {}, {}
+    for p in ps:
+        w = make_workload(490, lengths=[1536], num_q_heads=4, num_kv_heads=1, head_dim=128, g=4, p=p,
+                          outliers=True)
+        t = gp.prepare(w)
+        o = gp.attn(w, t)
+        torch.cuda.synchronize()
+        got[p] = o.cpu().numpy()
+        ref[p] = orc.attn_prefill(oracle_inputs(w))
+    means = {}
+    for p in ps:
+        mh, nh = orc.output_deviation(got[p], got[0.0])
+        mo, no = orc.output_deviation(ref[p], ref[0.0])
+        print(f"  p={p}: hip max={mh:.3e} mean={nh:.3e}   oracle max={mo:.3e} mean={no:.3e}")
+        if p == 0.0:
+            assert mh == 0.0 and nh == 0.0
+        assert abs(mh - mo) <= 2 * MAX_ABS
+        assert abs(nh - no) <= 0.05 * no + 1e-5
+        means[p] = nh
+    assert means[1.0] > means[0.1] > 0
+
+
 def _samples(w, rng, n):
     spans = orc.seq_spans(w.cu_seqlens)
     lens = [L for _, L in spans]

@@ -261,6 +261,34 @@ def test_pin_H_int8_scores_within_quantisation_bound():
             assert np.all(np.abs(s8 - s16) <= bound * (1 + 1e-9) + 1e-12)
 
 
+# ---------------------------------------------------------------- pin L
+def test_pin_L_output_deviation():
+    """MaxDiff / MeanDiff ([PL §5 Numerical Behavior], [PL App. G]): closed form
+    on a hand-worked pair; zero at 0 % INT8 coverage (the routed output is the
+    FP16 output); and at p > 0 bounded by the score perturbation: a softmax whose
+    scores move by at most e changes each weight by a factor within
+    [exp(-2e), exp(2e)], so |dO| <= (exp(2e) - 1) max|V|."""
+    mx, mn = orc.output_deviation(np.array([[1.0, 2.0], [3.0, 4.0]]), np.array([[1.0, 2.5], [2.0, 4.0]]))
+    assert mx == 1.0 and mn == 0.375
+    assert orc.output_deviation(np.zeros((0, 3)), np.zeros((0, 3))) == (0.0, 0.0)
+    lengths, hq, hk, d = [300, 130], 2, 1, 64
+    ref = orc.attn_prefill(oracle_inputs(_small(lengths, hq=hq, hk=hk, d=d, p=0.0, cfg=280, outliers=True)))
+    assert orc.output_deviation(ref, ref) == (0.0, 0.0)
+    for p in (0.3, 1.0):
+        w = _small(lengths, hq=hq, hk=hk, d=d, p=p, cfg=280, outliers=True)
+        inp = oracle_inputs(w)
+        out = orc.attn_prefill(inp)
+        mx, mn = orc.output_deviation(out, ref)
+        assert mx > 0 and 0 < mn <= mx
+        eps = 0.0
+        for b, (s0, L) in enumerate(orc.seq_spans(w.cu_seqlens)):
+            for h in range(hq):
+                eps = max(eps, float(np.max(np.abs(inp.routed_scores(b, h, 0, L, 0, L, 1) -
+                                                   inp.routed_scores(b, h, 0, L, 0, L, 0)))))
+        vmax = float(np.max(np.abs(w.v.astype(np.float64))))
+        assert mx <= (math.exp(2 * eps) - 1) * vmax
+
+
 # ---------------------------------------------------------------- pin I
 @pytest.mark.parametrize("g", [1, 2, 3, 16])
 def test_pin_I_packer_decoder(g):
