@@ -27,8 +27,11 @@ Conventions (all readings):
     per-block scales are ``float32 [H][B][ceil(max_seqlen/blk)]``; route words
     are ``uint64 [Hk][B][T]`` with ``T = ceil(max_seqlen/64)``;
   * GQA: query head hq reads KV head ``hq // (Hq // Hk)``;
-  * causal alignment is top-left (prefill, equal query/key lengths): key j is
-    legal for query i iff j <= i < L_b.
+  * causal alignment: a sequence's Lq queries are its last Lq positions of Lk
+    keys (bottom-right alignment; prefill is Lq = Lk): key j is legal for query
+    i iff j <= (Lk - Lq) + i and i < Lq.  Query tiles m count from the first
+    query, key tiles n from the first key; route words are ``[Hk][B][Tq]`` with
+    bits over key tiles.
 """
 from __future__ import annotations
 
@@ -111,23 +114,45 @@ def num_tiles(L: int) -> int:
 
 def tile_is_legal(m: int, n: int, Tb: int) -> bool:
     """Causal and sequence-boundary legality of score tile (m, n), independent of
-    routing ([PL §3 Preliminaries], [PL App. B])."""
+    routing ([PL §3 Preliminaries], [PL App. B]); prefill (Lq = Lk)."""
     return 0 <= n <= m < Tb
 
 
-def visit_matrix(cu_seqlens, max_seqlen: int, num_q_heads: int) -> np.ndarray:
-    """uint32 [B][Hq][T][T]: how often a correct kernel visits each score tile.
+def last_key_tile(m: int, Lq: int, Lk: int) -> int:
+    """Last key tile a query tile m may touch when the Lq queries are the last
+    Lq of Lk positions: the tile of key (Lk - Lq) + min(64 m + 63, Lq - 1).
+    Prefill (Lq = Lk) gives m."""
+    return ((Lk - Lq) + min(m * BLOCK_M + BLOCK_M - 1, Lq - 1)) // BLOCK_N
+
+
+def _pairs(cu_seqlens, cu_seqlens_k):
+    """Per sequence (Lq, Lk); cu_seqlens_k None means Lk = Lq."""
+    sq = seq_spans(cu_seqlens)
+    sk = sq if cu_seqlens_k is None else seq_spans(cu_seqlens_k)
+    if len(sk) != len(sq):
+        raise ValueError("cu_seqlens and cu_seqlens_k differ in batch")
+    out = []
+    for (_, Lq), (_, Lk) in zip(sq, sk):
+        if Lk < Lq:
+            raise ValueError("a sequence has more queries than keys")
+        out.append((Lq, Lk))
+    return out
+
+
+def visit_matrix(cu_seqlens, max_seqlen: int, num_q_heads: int, cu_seqlens_k=None,
+                 max_seqlen_k: Optional[int] = None) -> np.ndarray:
+    """uint32 [B][Hq][Tq][Tk]: how often a correct kernel visits each score tile.
 
     Every legal tile group is executed ([PL §3 Preliminaries]) and nothing else:
     1 on legal tiles, 0 elsewhere.
     """
-    spans = seq_spans(cu_seqlens)
-    T = num_tiles(max_seqlen)
-    out = np.zeros((len(spans), num_q_heads, T, T), dtype=np.uint32)
-    for b, (_, L) in enumerate(spans):
-        Tb = num_tiles(L)
-        for m in range(Tb):
-            out[b, :, m, : m + 1] = 1
+    pairs = _pairs(cu_seqlens, cu_seqlens_k)
+    Tq = num_tiles(max_seqlen)
+    Tk = num_tiles(max_seqlen if max_seqlen_k is None else max_seqlen_k)
+    out = np.zeros((len(pairs), num_q_heads, Tq, Tk), dtype=np.uint32)
+    for b, (Lq, Lk) in enumerate(pairs):
+        for m in range(num_tiles(Lq)):
+            out[b, :, m, : last_key_tile(m, Lq, Lk) + 1] = 1
     return out
 
 
@@ -136,7 +161,8 @@ def visit_matrix(cu_seqlens, max_seqlen: int, num_q_heads: int) -> np.ndarray:
 #     [PL §3 Preliminaries; PL §4; PL App. D; AN; GS]
 # ---------------------------------------------------------------------------
 
-def build_route_mask(tile_route: np.ndarray, cu_seqlens, max_seqlen: int, g: int) -> np.ndarray:
+def build_route_mask(tile_route: np.ndarray, cu_seqlens, max_seqlen: int, g: int, cu_seqlens_k=None,
+                     max_seqlen_k: Optional[int] = None) -> np.ndarray:
     """Pack per-tile decisions into one uint64 per (KV head, sequence, query-tile row).
 
     One bit governs a group of g adjacent key tiles and bit floor(n/g) selects
@@ -146,22 +172,25 @@ def build_route_mask(tile_route: np.ndarray, cu_seqlens, max_seqlen: int, g: int
     disagree); bits of groups with no legal tile, and whole rows past the
     sequence end, are 0.  More than 64 groups per row is an error.
 
-    tile_route: uint8 [Hk][B][T][T] (nonzero = INT8).  Returns uint64 [Hk][B][T].
+    tile_route: uint8 [Hk][B][Tq][Tk] (nonzero = INT8).  Returns uint64 [Hk][B][Tq].
+    With cu_seqlens_k (chunked prefill) the legal tiles of row m are
+    n <= last_key_tile(m, Lq, Lk).
     """
-    Hk, B, T, T2 = tile_route.shape
-    if T != T2 or T != num_tiles(max_seqlen):
-        raise ValueError("tile_route must be [Hk][B][T][T] with T = ceil(max_seqlen/64)")
-    if g < 1 or _cdiv(T, g) > 64:
+    Hk, B, Tq, Tk = tile_route.shape
+    Tk_want = num_tiles(max_seqlen if max_seqlen_k is None else max_seqlen_k)
+    if Tq != num_tiles(max_seqlen) or Tk != Tk_want:
+        raise ValueError("tile_route must be [Hk][B][Tq][Tk] with Tq, Tk = ceil(max_seqlen(_k)/64)")
+    if g < 1 or _cdiv(Tk, g) > 64:
         raise ValueError("more than 64 route groups per row")
-    spans = seq_spans(cu_seqlens)
-    words = np.zeros((Hk, B, T), dtype=np.uint64)
+    pairs = _pairs(cu_seqlens, cu_seqlens_k)
+    words = np.zeros((Hk, B, Tq), dtype=np.uint64)
     for hk in range(Hk):
-        for b, (_, L) in enumerate(spans):
-            Tb = num_tiles(L)
-            for m in range(Tb):
+        for b, (Lq, Lk) in enumerate(pairs):
+            for m in range(num_tiles(Lq)):
+                nl = last_key_tile(m, Lq, Lk)
                 w = 0
-                for j in range(m // g + 1):
-                    n0, n1 = j * g, min(j * g + g, m + 1)   # legal tiles of group j
+                for j in range(nl // g + 1):
+                    n0, n1 = j * g, min(j * g + g, nl + 1)   # legal tiles of group j
                     if all(int(tile_route[hk, b, m, n]) != 0 for n in range(n0, n1)):
                         w |= 1 << j
                 words[hk, b, m] = np.uint64(w)
@@ -174,18 +203,20 @@ def route_bit(word: int, n: int, g: int) -> int:
     return (int(word) >> (n // g)) & 1
 
 
-def decode_route_mask(words: np.ndarray, cu_seqlens, max_seqlen: int, g: int) -> np.ndarray:
-    """uint8 [Hk][B][T][T]: the decoded path of every legal tile, 0xFF on illegal tiles."""
-    Hk, B, T = words.shape
-    if T != num_tiles(max_seqlen):
-        raise ValueError("words must be [Hk][B][T]")
-    spans = seq_spans(cu_seqlens)
-    out = np.full((Hk, B, T, T), 0xFF, dtype=np.uint8)
+def decode_route_mask(words: np.ndarray, cu_seqlens, max_seqlen: int, g: int, cu_seqlens_k=None,
+                      max_seqlen_k: Optional[int] = None) -> np.ndarray:
+    """uint8 [Hk][B][Tq][Tk]: the decoded path of every legal tile, 0xFF on illegal tiles."""
+    Hk, B, Tq = words.shape
+    if Tq != num_tiles(max_seqlen):
+        raise ValueError("words must be [Hk][B][Tq]")
+    Tk = num_tiles(max_seqlen if max_seqlen_k is None else max_seqlen_k)
+    pairs = _pairs(cu_seqlens, cu_seqlens_k)
+    out = np.full((Hk, B, Tq, Tk), 0xFF, dtype=np.uint8)
     for hk in range(Hk):
-        for b, (_, L) in enumerate(spans):
-            for m in range(num_tiles(L)):
+        for b, (Lq, Lk) in enumerate(pairs):
+            for m in range(num_tiles(Lq)):
                 w = int(words[hk, b, m])
-                for n in range(m + 1):
+                for n in range(last_key_tile(m, Lq, Lk) + 1):
                     out[hk, b, m, n] = route_bit(w, n, g)
     return out
 
@@ -203,18 +234,25 @@ class AttnInputs:
     kv_int8 = True: ``k_q``, ``v_q`` int8 [N][Hk][d] with ``k_scale``, ``v_scale``
         float32 [Hk][B][nb64]; the effective key/value is ``int8 * scale``.
     Always: ``q`` fp16 [N][Hq][d]; ``q_q`` int8 and ``q_scale`` float32
-    [Hq][B][ceil(max_seqlen/blk_q)]; ``route_words`` uint64 [Hk][B][T].
+    [Hq][B][ceil(max_seqlen/blk_q)]; ``route_words`` uint64 [Hk][B][Tq].
+    Chunked prefill: ``cu_seqlens_k`` / ``max_seqlen_k`` describe the keys (K, V
+    and their scales are packed by them, Tk = ceil(max_seqlen_k/64) tiles);
+    None means the keys are the queries' own positions (prefill).
     """
 
     def __init__(self, *, q, cu_seqlens, max_seqlen, num_kv_heads, route_words, g, sm_scale,
                  q_q=None, q_scale=None, blk_q=64, k=None, v=None, k_q=None, k_scale=None,
-                 v_q=None, v_scale=None, kv_int8=False):
+                 v_q=None, v_scale=None, kv_int8=False, cu_seqlens_k=None, max_seqlen_k=None):
         self.q, self.k, self.v = q, k, v
         self.q_q, self.q_scale, self.k_q, self.k_scale = q_q, q_scale, k_q, k_scale
         self.v_q, self.v_scale = v_q, v_scale
         self.cu = np.asarray(cu_seqlens).astype(np.int64)
         self.spans = seq_spans(self.cu)
+        self.cu_k = self.cu if cu_seqlens_k is None else np.asarray(cu_seqlens_k).astype(np.int64)
+        self.spans_k = seq_spans(self.cu_k)
+        self.pairs = _pairs(self.cu, self.cu_k)
         self.max_seqlen = int(max_seqlen)
+        self.max_seqlen_k = int(max_seqlen if max_seqlen_k is None else max_seqlen_k)
         self.Hq = int(q.shape[1])
         self.Hk = int(num_kv_heads)
         self.d = int(q.shape[2])
@@ -231,10 +269,15 @@ class AttnInputs:
         """GQA: contiguous groups of Hq/Hk query heads share one KV head ([PL §4])."""
         return hq // (self.Hq // self.Hk)
 
+    def offset(self, b: int) -> int:
+        """Position of query 0 of sequence b among its keys: Lk - Lq."""
+        Lq, Lk = self.pairs[b]
+        return Lk - Lq
+
     def _kv(self, b: int, hk: int):
         key = (b, hk)
         if key not in self._kv_cache:
-            s0, L = self.spans[b]
+            s0, L = self.spans_k[b]
             nblk = num_tiles(L)
             if self.kv_int8:
                 ks = np.repeat(self.k_scale[hk, b, :nblk].astype(np.float64), BLOCK_N)[:L]
@@ -265,9 +308,9 @@ class AttnInputs:
         ([PL §3 Preliminaries], [AN], [GS]).  Reading: sm_scale is applied after
         dequantisation; Q is not pre-scaled before quantising.
         """
-        s0, _ = self.spans[b]
+        s0, _ = self.spans[b]              # query rows i are counted from the chunk start
         hk = self.kv_head(hq)
-        kf, _, k8, sk = self._kv(b, hk)
+        kf, _, k8, sk = self._kv(b, hk)    # key rows j from the sequence's first key
         if bit == 0:
             qf = self.q[s0 + i0:s0 + i1, hq].astype(np.float64)
             return self.sm * (qf @ kf[j0:j1].T)
@@ -277,10 +320,11 @@ class AttnInputs:
         return self.sm * sq[:, None] * sk[None, j0:j1] * s32.astype(np.float64)
 
 
-def attn_tile_row(inp: AttnInputs, b: int, hq: int, m: int) -> np.ndarray:
-    """Output rows of query tile m of (sequence b, query head hq), float64 [rows][d].
+def attn_tile_row(inp: AttnInputs, b: int, hq: int, m: int, with_lse: bool = False):
+    """Output rows of query tile m of (sequence b, query head hq), float64 [rows][d]
+    (with_lse: also the rows' log-sum-exp of the scores, natural log, [rows]).
 
-    Streams the legal key tiles n = 0..m in increasing order
+    Streams the legal key tiles n = 0..last_key_tile(m) in increasing order
     ([PL §3 Preliminaries]: the FlashAttention-style kernel iterates key tiles for
     each query tile and divides by the final normaliser).  For each tile the route
     bit picks the score path (O3/O4), then both paths update one shared state
@@ -288,10 +332,13 @@ def attn_tile_row(inp: AttnInputs, b: int, hq: int, m: int) -> np.ndarray:
 
         m' = max(m, rowmax s);  alpha = exp(m - m');  p = exp(s - m')
         l  <- alpha * l + rowsum p;  acc <- alpha * acc + p @ V_eff
-    and finally O = acc / l.  Initial m = -inf, l = 0, acc = 0.
+    and finally O = acc / l, LSE = m + log l.  Initial m = -inf, l = 0, acc = 0.
+    Query i sits at key position (Lk - Lq) + i (bottom-right alignment; 0 offset
+    in prefill).
     """
-    s0, L = inp.spans[b]
-    i0, i1 = m * BLOCK_M, min((m + 1) * BLOCK_M, L)
+    Lq, Lk = inp.pairs[b]
+    off = Lk - Lq
+    i0, i1 = m * BLOCK_M, min((m + 1) * BLOCK_M, Lq)
     if i0 >= i1:
         raise ValueError("query tile past sequence end")
     hk = inp.kv_head(hq)
@@ -301,33 +348,40 @@ def attn_tile_row(inp: AttnInputs, b: int, hq: int, m: int) -> np.ndarray:
     run_max = np.full(rows, -np.inf)
     run_sum = np.zeros(rows)
     acc = np.zeros((rows, inp.d))
-    qi = np.arange(i0, i1)[:, None]
-    for n in range(m + 1):
-        j0, j1 = n * BLOCK_N, min((n + 1) * BLOCK_N, L)
+    qpos = off + np.arange(i0, i1)[:, None]
+    for n in range(last_key_tile(m, Lq, Lk) + 1):
+        j0, j1 = n * BLOCK_N, min((n + 1) * BLOCK_N, Lk)
         bit = route_bit(word, n, inp.g)
         s = inp.routed_scores(b, hq, i0, i1, j0, j1, bit)
         kj = np.arange(j0, j1)[None, :]
-        s = np.where(kj <= qi, s, -np.inf)                      # causal legality
+        s = np.where(kj <= qpos, s, -np.inf)                    # causal legality
         new_max = np.maximum(run_max, s.max(axis=1))
         alpha = np.exp(run_max - new_max)
         p = np.exp(s - new_max[:, None])
         run_sum = alpha * run_sum + p.sum(axis=1)
         acc = alpha[:, None] * acc + p @ vf[j0:j1]
         run_max = new_max
-    return acc / run_sum[:, None]
+    out = acc / run_sum[:, None]
+    if with_lse:
+        return out, run_max + np.log(run_sum)
+    return out
 
 
-def attn_prefill(inp: AttnInputs) -> np.ndarray:
-    """Full routed causal prefill attention, float64 [N][Hq][d]."""
+def attn_prefill(inp: AttnInputs, with_lse: bool = False):
+    """Full routed causal attention of every query, float64 [N][Hq][d]
+    (with_lse: also the log-sum-exp of every query row's scores, [N][Hq])."""
     N = int(inp.cu[-1])
     out = np.zeros((N, inp.Hq, inp.d))
+    lse = np.zeros((N, inp.Hq))
     for b, (s0, L) in enumerate(inp.spans):
         for hq in range(inp.Hq):
             for m in range(num_tiles(L)):
                 i0, i1 = m * BLOCK_M, min((m + 1) * BLOCK_M, L)
-                out[s0 + i0:s0 + i1, hq] = attn_tile_row(inp, b, hq, m)
+                o, e = attn_tile_row(inp, b, hq, m, with_lse=True)
+                out[s0 + i0:s0 + i1, hq] = o
+                lse[s0 + i0:s0 + i1, hq] = e
         inp._kv_cache.clear()
-    return out
+    return (out, lse) if with_lse else out
 
 
 def attn_rows(inp: AttnInputs, samples: Sequence[Tuple[int, int, int]]) -> Dict[Tuple[int, int, int], np.ndarray]:
@@ -336,26 +390,26 @@ def attn_rows(inp: AttnInputs, samples: Sequence[Tuple[int, int, int]]) -> Dict[
 
 
 def s32_tiles(inp: AttnInputs, b: int, hq: int, m_begin: int, m_end: int) -> np.ndarray:
-    """int32 [m_end-m_begin][T][64][64]: the INT32 score tile of every INT8-routed
+    """int32 [m_end-m_begin][Tk][64][64]: the INT32 score tile of every INT8-routed
     legal tile of (b, hq), rows = query offset, cols = key offset within the tile.
 
     Entries for query or key positions past the sequence end are 0 (their
     operands are zero); tiles that are illegal or FP16-routed hold INT32_MIN.
     """
-    s0, L = inp.spans[b]
-    T = num_tiles(inp.max_seqlen)
-    Tb = num_tiles(L)
+    s0, _ = inp.spans[b]
+    Lq, Lk = inp.pairs[b]
+    Tk = num_tiles(inp.max_seqlen_k)
     hk = inp.kv_head(hq)
-    out = np.full((m_end - m_begin, T, BLOCK_M, BLOCK_N), INT32_MIN, dtype=np.int64)
+    out = np.full((m_end - m_begin, Tk, BLOCK_M, BLOCK_N), INT32_MIN, dtype=np.int64)
     _, _, k8, _ = inp._kv(b, hk)
-    for m in range(m_begin, min(m_end, Tb)):
+    for m in range(m_begin, min(m_end, num_tiles(Lq))):
         word = int(inp.words[hk, b, m])
-        i0, i1 = m * BLOCK_M, min((m + 1) * BLOCK_M, L)
+        i0, i1 = m * BLOCK_M, min((m + 1) * BLOCK_M, Lq)
         q8 = inp.q_q[s0 + i0:s0 + i1, hq].astype(np.int64)
-        for n in range(m + 1):
+        for n in range(last_key_tile(m, Lq, Lk) + 1):
             if route_bit(word, n, inp.g) != 1:
                 continue
-            j0, j1 = n * BLOCK_N, min((n + 1) * BLOCK_N, L)
+            j0, j1 = n * BLOCK_N, min((n + 1) * BLOCK_N, Lk)
             tile = np.zeros((BLOCK_M, BLOCK_N), dtype=np.int64)
             tile[: i1 - i0, : j1 - j0] = q8 @ k8[j0:j1].T
             out[m - m_begin, n] = tile
@@ -363,15 +417,15 @@ def s32_tiles(inp: AttnInputs, b: int, hq: int, m_begin: int, m_end: int) -> np.
 
 
 def route_used(inp: AttnInputs) -> np.ndarray:
-    """uint8 [B][Hq][T][T]: path taken per visited tile, 0xFF where not visited."""
-    T = num_tiles(inp.max_seqlen)
-    out = np.full((len(inp.spans), inp.Hq, T, T), 0xFF, dtype=np.uint8)
-    for b, (_, L) in enumerate(inp.spans):
+    """uint8 [B][Hq][Tq][Tk]: path taken per visited tile, 0xFF where not visited."""
+    Tq, Tk = num_tiles(inp.max_seqlen), num_tiles(inp.max_seqlen_k)
+    out = np.full((len(inp.spans), inp.Hq, Tq, Tk), 0xFF, dtype=np.uint8)
+    for b, (Lq, Lk) in enumerate(inp.pairs):
         for hq in range(inp.Hq):
             hk = inp.kv_head(hq)
-            for m in range(num_tiles(L)):
+            for m in range(num_tiles(Lq)):
                 w = int(inp.words[hk, b, m])
-                for n in range(m + 1):
+                for n in range(last_key_tile(m, Lq, Lk) + 1):
                     out[b, hq, m, n] = route_bit(w, n, inp.g)
     return out
 
@@ -380,34 +434,37 @@ def route_used(inp: AttnInputs) -> np.ndarray:
 # Independent formulations used to pin the streaming oracle
 # ---------------------------------------------------------------------------
 
-def attn_dense_two_pass(inp: AttnInputs, b: int, hq: int) -> np.ndarray:
+def attn_dense_two_pass(inp: AttnInputs, b: int, hq: int, with_lse: bool = False):
     """The same routed attention, materialised: the full L x L score matrix with each
     element taken from its tile's path, then a two-pass softmax (max, then
     normalised exponentials) and O = P V ([PL §3 Preliminaries]: S = QK^T,
-    P = softmax(S), O = PV).  float64 [L][d]."""
-    s0, L = inp.spans[b]
+    P = softmax(S), O = PV).  float64 [Lq][d] (with_lse: and log sum exp S, [Lq])."""
+    s0, _ = inp.spans[b]
+    Lq, Lk = inp.pairs[b]
     hk = inp.kv_head(hq)
     kf, vf, k8, sk = inp._kv(b, hk)
-    qf = inp.q[s0:s0 + L, hq].astype(np.float64)
+    qf = inp.q[s0:s0 + Lq, hq].astype(np.float64)
     S_fp = inp.sm * (qf @ kf.T)
     if inp.q_q is not None and k8 is not None:
-        q8 = inp.q_q[s0:s0 + L, hq].astype(np.int64)
-        sq = inp.q_scale[hq, b, np.arange(L) // inp.blk_q].astype(np.float64)
+        q8 = inp.q_q[s0:s0 + Lq, hq].astype(np.int64)
+        sq = inp.q_scale[hq, b, np.arange(Lq) // inp.blk_q].astype(np.float64)
         S_i8 = inp.sm * np.outer(sq, sk) * (q8 @ k8.T).astype(np.float64)
     else:
-        S_i8 = np.full((L, L), np.nan)
-    tile_i = np.arange(L) // BLOCK_M
-    tile_j = np.arange(L) // BLOCK_N
+        S_i8 = np.full((Lq, Lk), np.nan)
+    tile_i = np.arange(Lq) // BLOCK_M
+    tile_j = np.arange(Lk) // BLOCK_N
     words = np.array([int(w) for w in inp.words[hk, b]], dtype=object)
     # element (i, j) follows bit floor(tile_j / g) of word[tile_i]
-    bits = np.array([[(int(words[ti]) >> (tj // inp.g)) & 1 for tj in tile_j] for ti in range(num_tiles(L))])
-    R = bits[tile_i]                                      # [L][L]
+    bits = np.array([[(int(words[ti]) >> (tj // inp.g)) & 1 for tj in tile_j] for ti in range(num_tiles(Lq))])
+    R = bits[tile_i]                                      # [Lq][Lk]
     S = np.where(R == 1, S_i8, S_fp)
-    legal = np.arange(L)[None, :] <= np.arange(L)[:, None]
+    legal = np.arange(Lk)[None, :] <= (Lk - Lq) + np.arange(Lq)[:, None]
     S = np.where(legal, S, -np.inf)
     mx = S.max(axis=1, keepdims=True)
     E = np.exp(S - mx)
     P = E / E.sum(axis=1, keepdims=True)
+    if with_lse:
+        return P @ vf, mx[:, 0] + np.log(E.sum(axis=1))
     return P @ vf
 
 
@@ -415,25 +472,27 @@ def attn_brute_force(inp: AttnInputs, b: int, hq: int) -> List[List[float]]:
     """Element-by-element evaluation in plain Python for tiny L: each score from
     its own definition (route bit decoded per element, INT8 dot product summed
     as Python integers), then softmax of each row and the weighted sum of values."""
-    s0, L = inp.spans[b]
+    s0, _ = inp.spans[b]
+    k0, _ = inp.spans_k[b]
+    Lq, Lk = inp.pairs[b]
     d = inp.d
     hk = inp.kv_head(hq)
     sm = inp.sm
     out = []
-    for i in range(L):
+    for i in range(Lq):
         word = int(inp.words[hk, b, i // BLOCK_M])
         scores = []
-        for j in range(i + 1):
+        for j in range(Lk - Lq + i + 1):
             bit = (word >> ((j // BLOCK_N) // inp.g)) & 1
             if bit == 0:
                 if inp.kv_int8:
                     ks = float(inp.k_scale[hk, b, j // BLOCK_N])
-                    kvec = [float(inp.k_q[s0 + j, hk, c]) * ks for c in range(d)]
+                    kvec = [float(inp.k_q[k0 + j, hk, c]) * ks for c in range(d)]
                 else:
-                    kvec = [float(inp.k[s0 + j, hk, c]) for c in range(d)]
+                    kvec = [float(inp.k[k0 + j, hk, c]) for c in range(d)]
                 s = sm * sum(float(inp.q[s0 + i, hq, c]) * kvec[c] for c in range(d))
             else:
-                dot = sum(int(inp.q_q[s0 + i, hq, c]) * int(inp.k_q[s0 + j, hk, c]) for c in range(d))
+                dot = sum(int(inp.q_q[s0 + i, hq, c]) * int(inp.k_q[k0 + j, hk, c]) for c in range(d))
                 s = sm * float(inp.q_scale[hq, b, i // inp.blk_q]) * float(inp.k_scale[hk, b, j // BLOCK_N]) * dot
             scores.append(s)
         mx = max(scores)
@@ -442,11 +501,11 @@ def attn_brute_force(inp: AttnInputs, b: int, hq: int) -> List[List[float]]:
         row = []
         for c in range(d):
             acc = 0.0
-            for j in range(i + 1):
+            for j in range(len(scores)):
                 if inp.kv_int8:
-                    vv = float(inp.v_q[s0 + j, hk, c]) * float(inp.v_scale[hk, b, j // BLOCK_N])
+                    vv = float(inp.v_q[k0 + j, hk, c]) * float(inp.v_scale[hk, b, j // BLOCK_N])
                 else:
-                    vv = float(inp.v[s0 + j, hk, c])
+                    vv = float(inp.v[k0 + j, hk, c])
                 acc += e[j] * vv
             row.append(acc / z)
         out.append(row)

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle as orc
-from workloads import config, make_workload, cu_from_lengths, legal_tile_matrix
+from workloads import config, make_workload, make_chunked_workload, cu_from_lengths, legal_tile_matrix
 from tests.oracle_inputs import oracle_inputs, words_from_group_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -287,6 +287,82 @@ def test_pin_L_output_deviation():
                                                    inp.routed_scores(b, h, 0, L, 0, L, 0)))))
         vmax = float(np.max(np.abs(w.v.astype(np.float64))))
         assert mx <= (math.exp(2 * eps) - 1) * vmax
+
+
+# ---------------------------------------------------------------- pin M
+@pytest.mark.parametrize("kv_int8,blk_q", [(False, 64), (False, 128), (True, 64)])
+def test_pin_M_chunk_rows_equal_prefill_rows(kv_int8, blk_q):
+    """Chunked prefill with bottom-right alignment: when each chunk starts on a Q
+    block boundary, its queries see exactly the keys, scales and routes the same
+    positions see in a full prefill, so its rows equal the prefill's rows bit for
+    bit (the streaming order is the same)."""
+    lengths_k = [640, 300, 256]
+    lengths_q = [200, 44, 256]          # offsets 440 -> rounded below to blocks
+    lengths_q = [L - ((L - q + 127) // 128) * 128 for L, q in zip(lengths_k, lengths_q)]
+    full = make_workload(290, lengths=lengths_k, num_q_heads=4, num_kv_heads=2, head_dim=64, g=2, p=0.5,
+                         outliers=True, kv_int8=kv_int8, blk_q=blk_q)
+    chunk = make_chunked_workload(290, lengths_q=lengths_q, lengths_k=lengths_k, num_q_heads=4, num_kv_heads=2,
+                                  head_dim=64, g=2, p=0.5, outliers=True, kv_int8=kv_int8, blk_q=blk_q)
+    fin = oracle_inputs(full)
+    ref = orc.attn_prefill(fin)
+    # the chunk's route words: the full words of the same query-tile rows
+    words = np.zeros((2, 3, chunk.T), dtype=np.uint64)
+    for b, (Lq, Lk) in enumerate(zip(lengths_q, lengths_k)):
+        off = (Lk - Lq) // 64
+        words[:, b, : (Lq + 63) // 64] = fin.words[:, b, off: off + (Lq + 63) // 64]
+    out = orc.attn_prefill(oracle_inputs(chunk, route_words=words))
+    for b, (Lq, Lk) in enumerate(zip(lengths_q, lengths_k)):
+        s0q, s0k = int(chunk.cu_seqlens[b]), int(full.cu_seqlens[b])
+        assert np.array_equal(out[s0q:s0q + Lq], ref[s0k + Lk - Lq:s0k + Lk])
+
+
+def test_pin_M_chunked_dense_brute_force_and_lse():
+    """Chunked prefill and decode (Lq = 1) against the materialised two-pass
+    formulation and the element-by-element brute force; the log-sum-exp against
+    the two-pass one and, for the very first query of a prefill, the closed form
+    LSE = s_00 (its only key)."""
+    w = make_chunked_workload(291, lengths_q=[70, 1, 5], lengths_k=[200, 77, 5], num_q_heads=2, num_kv_heads=1,
+                              head_dim=64, g=1, p=0.5, outliers=True)
+    inp = oracle_inputs(w)
+    out, lse = orc.attn_prefill(inp, with_lse=True)
+    for b, (s0, Lq) in enumerate(orc.seq_spans(w.cu_seqlens)):
+        for h in range(2):
+            o2, l2 = orc.attn_dense_two_pass(inp, b, h, with_lse=True)
+            assert np.allclose(out[s0:s0 + Lq, h], o2, rtol=0, atol=1e-12)
+            assert np.allclose(lse[s0:s0 + Lq, h], l2, rtol=0, atol=1e-12)
+    bf = np.array(orc.attn_brute_force(inp, 1, 1))          # decode: one query over 77 keys
+    assert np.allclose(out[70:71, 1], bf, rtol=0, atol=1e-12)
+    bf = np.array(orc.attn_brute_force(inp, 2, 0))          # Lq = Lk: plain prefill rows
+    assert np.allclose(out[71:76, 0], bf, rtol=0, atol=1e-12)
+    # sequence 2 has Lq = Lk: query 0 sees only key 0, so LSE = its score
+    s00 = inp.routed_scores(2, 0, 0, 1, 0, 1, orc.route_bit(int(inp.words[0, 2, 0]), 0, 1))[0, 0]
+    assert lse[71, 0] == s00
+
+
+def test_pin_M_chunked_legality_and_packer():
+    """Visit matrix = brute-force legality (tile (m, n) holds a pair j <= off + i);
+    the packer ANDs exactly the legal tiles of each group."""
+    Lq, Lk = [100, 1, 64], [300, 129, 64]
+    cu_q, cu_k = cu_from_lengths(Lq), cu_from_lengths(Lk)
+    vis = orc.visit_matrix(cu_q, max(Lq), 1, cu_k, max(Lk))
+    for b in range(3):
+        for m in range(vis.shape[2]):
+            for n in range(vis.shape[3]):
+                legal = any(j <= Lk[b] - Lq[b] + i for i in range(m * 64, min(m * 64 + 64, Lq[b]))
+                            for j in range(n * 64, min(n * 64 + 64, Lk[b])))
+                assert vis[b, 0, m, n] == int(legal)
+    rng = np.random.default_rng(5)
+    tr = rng.integers(0, 2, size=(1, 3, vis.shape[2], vis.shape[3])).astype(np.uint8)
+    for g in (1, 2, 3):
+        words = orc.build_route_mask(tr, cu_q, max(Lq), g, cu_k, max(Lk))
+        for b in range(3):
+            for m in range(vis.shape[2]):
+                want = 0
+                for j in range((vis.shape[3] + g - 1) // g):
+                    tiles = [n for n in range(j * g, min(j * g + g, vis.shape[3])) if vis[b, 0, m, n]]
+                    if tiles and all(tr[0, b, m, n] for n in tiles):
+                        want |= 1 << j
+                assert int(words[0, b, m]) == want
 
 
 # ---------------------------------------------------------------- pin I

@@ -61,6 +61,10 @@ class Workload:
     kv_int8: bool = False    # K/V consumed as an INT8 cache
     sm_scale: float = 0.0    # fp32 value of 1/sqrt(d)
     notes: str = ""
+    # chunked prefill: the keys (K, V rows) per sequence; None = the queries' own
+    # positions.  The queries are then the last Lq of each sequence's Lk positions.
+    cu_seqlens_k: Optional[np.ndarray] = None
+    max_seqlen_k: Optional[int] = None
 
     @property
     def batch(self) -> int:
@@ -77,6 +81,14 @@ class Workload:
     @property
     def T(self) -> int:
         return (self.max_seqlen + TILE - 1) // TILE
+
+    @property
+    def T_k(self) -> int:
+        return ((self.max_seqlen_k or self.max_seqlen) + TILE - 1) // TILE
+
+    @property
+    def lengths_k(self) -> np.ndarray:
+        return self.lengths if self.cu_seqlens_k is None else np.diff(self.cu_seqlens_k.astype(np.int64))
 
 
 def fp32_inv_sqrt(d: int) -> float:
@@ -185,6 +197,50 @@ def make_workload(cfg_id: int, *, lengths, num_q_heads: int, num_kv_heads: int, 
                     max_seqlen=max_seqlen, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                     head_dim=head_dim, g=g, blk_q=blk_q, tile_route=tr, kv_int8=kv_int8,
                     sm_scale=fp32_inv_sqrt(head_dim), notes=notes)
+
+
+def chunk_legal_tiles(Lq: int, Lk: int, Tq: int, Tk: int) -> np.ndarray:
+    """bool [Tq][Tk]: tiles a query tile touches when the Lq queries are the last
+    Lq of Lk positions (key j allowed for query i iff j <= Lk - Lq + i)."""
+    out = np.zeros((Tq, Tk), dtype=bool)
+    for m in range((Lq + TILE - 1) // TILE):
+        last_q = min(m * TILE + TILE - 1, Lq - 1)
+        out[m, : (Lk - Lq + last_q) // TILE + 1] = True
+    return out
+
+
+def make_chunked_workload(cfg_id: int, *, lengths_q, lengths_k, num_q_heads: int, num_kv_heads: int,
+                          head_dim: int, g: int, blk_q: int = 64, p: float = 0.5, outliers: bool = False,
+                          kv_int8: bool = False, name: str = "") -> Workload:
+    """Chunked prefill / decode: sequence b has Lk_b keys and its last Lq_b
+    positions are the queries.  Q rows are those positions' rows of the Q that
+    make_workload(cfg_id, lengths=lengths_k, ...) draws, so a chunk's inputs
+    equal the matching rows of the full prefill's.  Routes: Bernoulli(p) per
+    legal tile group of [Hk][B][Tq][Tk], drawn from the route stream."""
+    lengths_q = [int(x) for x in lengths_q]
+    lengths_k = [int(x) for x in lengths_k]
+    assert len(lengths_q) == len(lengths_k) and all(0 < a <= b for a, b in zip(lengths_q, lengths_k))
+    cu_k = cu_from_lengths(lengths_k)
+    cu_q = cu_from_lengths(lengths_q)
+    Nk = int(cu_k[-1])
+    oc = outlier_channels(cfg_id, head_dim) if outliers else None
+    q_full = _normal_fp16(rng_for(cfg_id, S_Q), (Nk, num_q_heads, head_dim), oc, Q_OUTLIER_SCALE)
+    k = _normal_fp16(rng_for(cfg_id, S_K), (Nk, num_kv_heads, head_dim), oc, K_OUTLIER_SCALE)
+    v = _normal_fp16(rng_for(cfg_id, S_V), (Nk, num_kv_heads, head_dim), None)
+    q = np.concatenate([q_full[int(cu_k[b + 1]) - Lq:int(cu_k[b + 1])] for b, Lq in enumerate(lengths_q)], axis=0)
+    max_q, max_k = max(lengths_q), max(lengths_k)
+    Tq, Tk = (max_q + TILE - 1) // TILE, (max_k + TILE - 1) // TILE
+    rng = rng_for(cfg_id, S_ROUTE)
+    ngroups = (Tk + g - 1) // g
+    u = rng.random(size=(num_kv_heads, len(lengths_q), Tq, ngroups))
+    tiles = np.repeat((u < p).astype(np.uint8), g, axis=3)[..., :Tk]
+    tr = np.zeros((num_kv_heads, len(lengths_q), Tq, Tk), dtype=np.uint8)
+    for b, (Lq, Lk) in enumerate(zip(lengths_q, lengths_k)):
+        tr[:, b] = np.where(chunk_legal_tiles(Lq, Lk, Tq, Tk)[None], tiles[:, b], 0)
+    return Workload(name=name or f"chunk{cfg_id}", cfg_id=cfg_id, q=q, k=k, v=v, cu_seqlens=cu_q,
+                    max_seqlen=max_q, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                    g=g, blk_q=blk_q, tile_route=tr, kv_int8=kv_int8, sm_scale=fp32_inv_sqrt(head_dim),
+                    cu_seqlens_k=cu_k, max_seqlen_k=max_k)
 
 
 def varlen_lengths(cfg_id: int, count: int = 16, lo: int = 512, hi: int = 8192):
