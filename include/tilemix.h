@@ -10,7 +10,8 @@
  *            Matrix, Reaching 2.22x FlashAttention Throughput for 4K Prefill on A100".
  *   [GS]     gist.science technical summary, "Resumen Tecnico", subsection on
  *            compact bitmask routing.
- *   [AF]     ai-feeds.com summary (Chinese), section on interfaces to existing products.
+ *   [AF]     ai-feeds.com summary (Chinese), sections on interfaces to existing products
+ *            and on limitations.
  *
  * Conventions shared by every call:
  *   - Every pointer argument is a DEVICE pointer unless marked "host".
@@ -23,6 +24,13 @@
  *     decreasing, every length <= max_seqlen.  A fixed-length batch is
  *     cu_seqlens = {0, L, 2L, ...}.
  *   - Score tiles are 64 x 64 (query tile m, key tile n); T = ceil(max_seqlen/64).
+ *   - Chunked prefill / decode (optional key prefix sums `cu_seqlens_k` with
+ *     `max_seqlen_k` > 0): sequence b has Lq_b = cu_seqlens[b+1] - cu_seqlens[b]
+ *     queries and Lk_b >= Lq_b keys, and its queries are the last Lq_b of its Lk_b
+ *     positions (bottom-right causal alignment): key j is legal for query i iff
+ *     j <= (Lk_b - Lq_b) + i.  Query tiles count from the first query, key tiles
+ *     from the first key, Tk = ceil(max_seqlen_k/64).  Without cu_seqlens_k
+ *     (max_seqlen_k = 0) the keys are the queries' own positions (prefill, Tk = T).
  *   - Arguments are validated on the host before any launch.  On failure a
  *     status other than TILEMIX_OK is returned, nothing is launched and
  *     tilemix_last_error() describes the problem.  A failed HIP launch returns
@@ -90,33 +98,37 @@ int32_t tilemix_quantize_blockwise(const void* x, int64_t stride_tok, int64_t st
  * [PL App. D], [AN]).  One bit governs a group of g adjacent key tiles; bit
  * j covers key tiles [j*g, j*g + g) and bit 0 is the least significant.
  *
- *   tile_route  uint8 [num_kv_heads][batch][T][T]; nonzero = INT8, 0 = FP16.
- *               Entries of illegal tiles (n > m, or m past the sequence end)
- *               are ignored.
+ *   tile_route  uint8 [num_kv_heads][batch][T][Tk]; nonzero = INT8, 0 = FP16.
+ *               Entries of illegal tiles (keys after every query of the row,
+ *               or m past the sequence end) are ignored.
+ *   cu_seqlens_k, max_seqlen_k: key prefix sums and bound for chunked prefill
+ *               (see the conventions above), or NULL and 0 for prefill.
  *   route_words uint64 [num_kv_heads][batch][T] (written).  A group's bit is the
  *               AND of its legal tiles' decisions (FP16 wins when they
  *               disagree); bits of groups with no legal tile and rows past the
  *               sequence end are 0.
- *   g           >= 1 with ceil(T/g) <= 64, else TILEMIX_ERR_TOO_MANY_GROUPS.
+ *   g           >= 1 with ceil(Tk/g) <= 64, else TILEMIX_ERR_TOO_MANY_GROUPS.
  */
 int32_t tilemix_build_route_mask(const uint8_t* tile_route, const int32_t* cu_seqlens,
-                                 int32_t batch, int32_t max_seqlen, int32_t num_kv_heads, int32_t g,
+                                 const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen,
+                                 int32_t max_seqlen_k, int32_t num_kv_heads, int32_t g,
                                  uint64_t* route_words, void* stream);
 
 /*
  * Inverse of the packer, for bit-exact checks: decode R = (word >> floor(n/g)) & 1
  * for every tile ([GS], [PL §3 Preliminaries]).
- *   tile_route_out uint8 [num_kv_heads][batch][T][T] (written): legal tiles get
+ *   tile_route_out uint8 [num_kv_heads][batch][T][Tk] (written): legal tiles get
  *                  their bit (1 = INT8), illegal tiles 0xFF.
  */
 int32_t tilemix_decode_route_mask(const uint64_t* route_words, const int32_t* cu_seqlens,
-                                  int32_t batch, int32_t max_seqlen, int32_t num_kv_heads, int32_t g,
+                                  const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen,
+                                  int32_t max_seqlen_k, int32_t num_kv_heads, int32_t g,
                                   uint8_t* tile_route_out, void* stream);
 
 /* Host struct: problem description of one attention call. */
 typedef struct {
   int32_t batch;        /* sequences, >= 1 */
-  int32_t max_seqlen;   /* >= every sequence length, >= 1 */
+  int32_t max_seqlen;   /* >= every sequence's query count, >= 1 */
   int32_t num_q_heads;  /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads; /* Hk, 1..256 */
   int32_t head_dim;     /* 64 or 128 */
@@ -133,6 +145,13 @@ typedef struct {
                            q and k, with the same definition and bit-identical results;
                            q_q, q_scale, k_q and k_scale are not read (may be NULL).
                            Requires kv_int8 = 0. */
+  int32_t max_seqlen_k; /* 0: prefill, the keys are the queries' positions.  > 0: chunked
+                           prefill / decode over a KV cache (an extension: the pages scope
+                           the method to prefill, [PL Limitations], and list decode as not
+                           yet evaluated, [AN], [AF]): >= every key count and
+                           >= max_seqlen, with tensors.cu_seqlens_k; K, V, k_q and their
+                           scales are packed by cu_seqlens_k, route words index query-tile
+                           rows with bits over ceil(max_seqlen_k/64) key tiles. */
 } tilemix_attn_params;
 
 /* Host struct of device pointers for one attention call. */
@@ -147,11 +166,15 @@ typedef struct {
   const float* q_scale;   /* float32 [Hq][batch][ceil(max_seqlen/blk_q)]; unused when otf_quant = 1 */
   const int8_t* k_q;      /* kv_int8 = 0: int8 [N][Hk][d] contiguous (quantize_blockwise(k, 64));
                              unused when kv_int8 = 1 or otf_quant = 1 */
-  const float* k_scale;   /* float32 [Hk][batch][T]: per 64-token block of K; unused when otf_quant = 1 */
-  const float* v_scale;   /* kv_int8 = 1: float32 [Hk][batch][T]; 0: unused */
-  const int32_t* cu_seqlens;     /* int32 [batch+1] */
+  const float* k_scale;   /* float32 [Hk][batch][Tk]: per 64-token block of K; unused when otf_quant = 1 */
+  const float* v_scale;   /* kv_int8 = 1: float32 [Hk][batch][Tk]; 0: unused */
+  const int32_t* cu_seqlens;     /* int32 [batch+1]: queries (and keys, in prefill) */
   const uint64_t* route_words;   /* uint64 [Hk][batch][T] from tilemix_build_route_mask */
   void* out;              /* fp16 or float32 [N][Hq][d] contiguous (written) */
+  const int32_t* cu_seqlens_k;   /* int32 [batch+1] key prefix sums when max_seqlen_k > 0, else NULL */
+  float* lse;             /* optional (NULL = not written): float32 [N][Hq], natural-log
+                             log-sum-exp of each query row's scores s_ij, for merging
+                             partial attentions */
 } tilemix_attn_tensors;
 
 /* Host: bytes of device workspace tilemix_attn_prefill needs for `params`. */
@@ -173,7 +196,8 @@ int32_t tilemix_attn_workspace_size(const tilemix_attn_params* params, size_t* b
  * Both paths update one online-softmax state per query row (running max, sum
  * and output accumulator in fp32); P.V runs in fp16 with fp32 accumulation
  * (kv_int8 = 1: v = v_int8 * v_scale, the scale folded into P); the output is
- * acc / sum.  Key j is legal for query i iff j <= i < L_b (top-left causal).
+ * acc / sum.  Key j is legal for query i iff j <= i < L_b (top-left causal), or
+ * with cu_seqlens_k iff j <= (Lk_b - Lq_b) + i (chunked prefill; decode is Lq_b = 1).
  *
  * `workspace` must hold tilemix_attn_workspace_size() bytes (256-byte aligned);
  * it receives the varlen/GQA work list, rebuilt on every call.  Equivalent to
@@ -184,15 +208,16 @@ int32_t tilemix_attn_prefill(const tilemix_attn_params* params, const tilemix_at
 
 /*
  * The varlen/GQA work schedule alone ([PL §4]: prefix-sum metadata,
- * padding-free execution): from cu_seqlens (device int32 [batch+1]) it writes
+ * padding-free execution): from cu_seqlens (device int32 [batch+1]; with
+ * cu_seqlens_k for chunked prefill, NULL otherwise, as in the tensors) it writes
  * the work list of (sequence, KV head, query tile, head chunk) items into
  * `workspace`, longest causal rows first, each (sequence, KV head) group kept
  * on one XCD where the slots allow.  Asynchronous on `stream`; no allocation.
  * The list depends only on `params` and cu_seqlens, so several layers of one
  * batch may share it.
  */
-int32_t tilemix_attn_plan(const tilemix_attn_params* params, const int32_t* cu_seqlens, void* workspace,
-                          size_t workspace_bytes, void* stream);
+int32_t tilemix_attn_plan(const tilemix_attn_params* params, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_k, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The attention of tilemix_attn_prefill over the work list a previous
@@ -207,10 +232,10 @@ int32_t tilemix_attn_run(const tilemix_attn_params* params, const tilemix_attn_t
 /* Host struct: debug products of tilemix_attn_prefill_debug (device pointers, any may be NULL). */
 typedef struct {
   int32_t seq, q_head, m_begin, m_end;  /* window of query-tile rows whose INT32 tiles are dumped */
-  int32_t* s32_tiles;      /* int32 [m_end-m_begin][T][64][64] (query offset, key offset):
+  int32_t* s32_tiles;      /* int32 [m_end-m_begin][Tk][64][64] (query offset, key offset):
                               raw INT32 score tile of every INT8-routed tile; others INT32_MIN */
-  uint32_t* visit_count;   /* uint32 [batch][Hq][T][T]: +1 per tile visit (zeroed by the call) */
-  uint8_t* route_used;     /* uint8 [batch][Hq][T][T]: path taken, 0xFF if not visited */
+  uint32_t* visit_count;   /* uint32 [batch][Hq][T][Tk]: +1 per tile visit (zeroed by the call) */
+  uint8_t* route_used;     /* uint8 [batch][Hq][T][Tk]: path taken, 0xFF if not visited */
 } tilemix_debug;
 
 /* Same computation and output as tilemix_attn_prefill, plus the debug products

@@ -3,7 +3,9 @@
 // Method (paperlayer.ai summary of arXiv 2608.17336, "TileMix: Tile-Centric
 // Mixed-Precision Attention for LLM Inference Acceleration": §1, §3
 // Preliminaries, §4, App. C; ainews.surl.tw article on TileMix): for each query
-// tile the legal key tiles are streamed; a bit of the row's packed 64-bit word,
+// tile the legal key tiles are streamed (chunked prefill: the Lq queries are
+// the last Lq of Lk positions, so a query tile's keys start (Lk - Lq) earlier
+// and the causal edge may cut two tiles); a bit of the row's packed 64-bit word,
 // (w >> floor(n/g)) & 1, sends tile n through an FP16 or an INT8 QK^T (INT32
 // accumulation, then the block scales); both update one online-softmax state
 // (running max, sum, output accumulator) and P.V runs in FP16.
@@ -403,7 +405,11 @@ void attn_prefill_kernel(const AttnArgs a) {
   const int c = lane & 15;           // query column / operand row inside a 16-block
   const int gq = lane >> 4;          // lane group 0..3
   const int seq0 = uniform(a.cu[b]);
-  const int L = uniform(a.cu[b + 1]) - seq0;
+  const int L = uniform(a.cu[b + 1]) - seq0;                     // queries of this sequence
+  const int kseq0 = a.cu_k ? uniform(a.cu_k[b]) : seq0;          // its first key row
+  const int Lk = a.cu_k ? uniform(a.cu_k[b + 1]) - kseq0 : L;    // its keys
+  const int qoff = Lk - L;                                       // key position of query 0
+  const int n_last = last_key_tile(m, L, Lk);                    // last key tile of this row
   const int h_begin = chunk * a.hc;
   const int nh = min(a.hc, a.G - h_begin);   // heads in this chunk = q-blocks per wave
 
@@ -463,19 +469,19 @@ void attn_prefill_kernel(const AttnArgs a) {
     }
   }
 
-  // ---- sources: this sequence's rows of KV head hk.  Per tile the buffer
+  // ---- sources: this sequence's key rows of KV head hk.  Per tile the buffer
   // base moves to the tile's first row and the range shrinks to the rows left,
-  // so rows >= L read as zero.
+  // so rows >= Lk read as zero.
   const int64_t esz = KVI8 ? 1 : 2;
-  const char* kbase = static_cast<const char*>(a.k) + ((int64_t)seq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
-  const char* vbase = static_cast<const char*>(a.v) + ((int64_t)seq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
+  const char* kbase = static_cast<const char*>(a.k) + ((int64_t)kseq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
+  const char* vbase = static_cast<const char*>(a.v) + ((int64_t)kseq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
   const uint32_t kv_stride = (uint32_t)(a.kv_st * esz);
   const uint32_t k8_stride = KVI8 ? kv_stride : (uint32_t)(a.Hk * D);
   const char* k8base =
-      (KVI8 || OTF) ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)seq0 * a.Hk + hk) * D);
+      (KVI8 || OTF) ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)kseq0 * a.Hk + hk) * D);
   // (empty: a zero-length range, the load reads zeros and touches no memory)
   auto tile_rsrc = [&](const char* base, uint32_t stride, int n, bool empty) __attribute__((always_inline)) {
-    const int rows = empty ? 0 : max(L - n * kTile, 0);
+    const int rows = empty ? 0 : max(Lk - n * kTile, 0);
     return make_rsrc(base + (int64_t)n * kTile * stride, (uint32_t)rows * stride);
   };
   typename A::Dma dma;
@@ -486,8 +492,8 @@ void attn_prefill_kernel(const AttnArgs a) {
   // per-tile scales through the scalar cache (a vector load would be counted
   // behind the tile loads in flight, and waiting for it would wait for them)
   typedef const __attribute__((address_space(4))) float cfloat;
-  cfloat* kscale_row = OTF ? nullptr : (cfloat*)(a.k_scale + ((int64_t)hk * a.batch + b) * a.T);
-  cfloat* vscale_row = KVI8 ? (cfloat*)(a.v_scale + ((int64_t)hk * a.batch + b) * a.T) : nullptr;
+  cfloat* kscale_row = OTF ? nullptr : (cfloat*)(a.k_scale + ((int64_t)hk * a.batch + b) * a.Tk);
+  cfloat* vscale_row = KVI8 ? (cfloat*)(a.v_scale + ((int64_t)hk * a.batch + b) * a.Tk) : nullptr;
   // Route of tile n = bit floor(n/g) of the word, tracked incrementally:
   // bit 0 of wsh is the current tile's group, `left` counts the tiles the
   // group still covers (groups past bit 63 shift in zeros = FP16).
@@ -561,12 +567,15 @@ void attn_prefill_kernel(const AttnArgs a) {
   // read in step n-1; after the last tile they read nothing), then tile n is
   // computed from its stage in two 32-key halves, and the loads are awaited
   // before the barrier.  One body serves every tile; only the QK^T path and
-  // the diagonal mask branch (uniformly) inside it.  The loop runs two tiles
+  // the causal-edge mask branch (uniformly) inside it.  The loop runs two tiles
   // per iteration so each stage is a fixed LDS object.
   auto tile = [&](int n, const char* cur, char* next) __attribute__((always_inline)) {
     const int rc = (int)(wsh & 1);
     const int rnext = (left == 1) ? (int)((wsh >> 1) & 1) : rc;
-    const bool last = (n == m);
+    const bool last = (n == n_last);
+    // a key of this tile may come after the tile's first query (the diagonal
+    // tile in prefill; up to two tiles on a chunk's causal edge)
+    const bool edge = n * kTile + kTile - 1 > qoff + m * kTile;
     const char* kl = cur;
     const char* vl = cur + A::KBYTES;
     typename A::Stage st;
@@ -600,7 +609,7 @@ void attn_prefill_kernel(const AttnArgs a) {
       for (int j = 0; j < QB; ++j) {
         const int qbi = wave * nh + j;
         if (j < nh && (qbi & 3) == 0 && lane == 0) {
-          const int64_t t = (((int64_t)b * a.Hq + qb_head(j)) * a.T + m) * a.T + n;
+          const int64_t t = (((int64_t)b * a.Hq + qb_head(j)) * a.T + m) * a.Tk + n;
           if (a.dbg_visits) atomicAdd(a.dbg_visits + t, 1u);
           if (a.dbg_route) a.dbg_route[t] = (uint8_t)rc;
         }
@@ -620,7 +629,7 @@ void attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
           for (int j = 0; j < QB; ++j) {
             if (j < nh && b == a.dbg_seq && qb_head(j) == a.dbg_head && m >= a.dbg_m0 && m < a.dbg_m1 && a.dbg_s32) {
-              int32_t* dst = a.dbg_s32 + ((((int64_t)(m - a.dbg_m0) * a.T + n) * kTile + qb_row(j)) * kTile);
+              int32_t* dst = a.dbg_s32 + ((((int64_t)(m - a.dbg_m0) * a.Tk + n) * kTile + qb_row(j)) * kTile);
 #pragma unroll
               for (int kk = 0; kk < 2; ++kk)
                 *reinterpret_cast<i32x4*>(dst + (2 * h + kk) * 16 + gq * 4) = S[j][kk];
@@ -629,10 +638,10 @@ void attn_prefill_kernel(const AttnArgs a) {
         }
         A::int_to_float_bits(S);
       }
-      if (last) {
+      if (edge) {
         int qpos[QB];
 #pragma unroll
-        for (int j = 0; j < QB; ++j) qpos[j] = m * kTile + qb_row(j);
+        for (int j = 0; j < QB; ++j) qpos[j] = qoff + m * kTile + qb_row(j);
         A::mask_diag(S, n * kTile + 32 * h + 4 * gq, qpos);
       }
       __builtin_amdgcn_s_setprio(0);
@@ -658,9 +667,9 @@ void attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll 1
   for (int n = 0;; n += 2) {
     tile(n, stA, stB);
-    if (n + 1 > m) break;
+    if (n + 1 > n_last) break;
     tile(n + 1, stB, stA);
-    if (n + 2 > m) break;
+    if (n + 2 > n_last) break;
   }
 
   // ---- epilogue: O = acc / l
@@ -673,6 +682,9 @@ void attn_prefill_kernel(const AttnArgs a) {
     const float inv = 1.0f / l;
     if (!qb_valid(j)) continue;
     const int64_t tok = (int64_t)seq0 + m * kTile + qb_row(j);
+    // log-sum-exp of the row's scores: the state is in log2 units of the
+    // scaled scores, so LSE = (m_ref + log2 l) ln 2
+    if (a.lse && gq == 0) a.lse[tok * a.Hq + qb_head(j)] = (mref[j] + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
     const int64_t base = (tok * a.Hq + qb_head(j)) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

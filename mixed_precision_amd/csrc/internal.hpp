@@ -26,8 +26,17 @@ struct RouteArgs {
   uint64_t* words_out;
   uint8_t* tile_route_out;
   const int32_t* cu;
-  int32_t batch, T, num_kv_heads, g;
+  const int32_t* cu_k;   // key prefix sums (chunked prefill), or nullptr: keys = queries
+  int32_t batch, T, Tk, num_kv_heads, g;   // T query tiles, Tk key tiles
 };
+
+// Last key tile that query tile m reaches when the Lq queries are the last Lq of
+// Lk positions (bottom-right causal alignment; prefill has Lq = Lk and gives m).
+__host__ __device__ inline int last_key_tile(int m, int Lq, int Lk) {
+  const int q = m * kTile + kTile - 1 < Lq - 1 ? m * kTile + kTile - 1 : Lq - 1;
+  const int r = (Lk - Lq) + q;
+  return r < 0 ? 0 : r / kTile;
+}
 
 // Work item of the fused kernel: one query-tile row m of one sequence b for one
 // chunk of the query heads that share KV head hk.  b < 0 marks an empty slot.
@@ -53,10 +62,13 @@ struct AttnArgs {
   const float* k_scale;
   const float* v_scale;
   const int32_t* cu;
+  const int32_t* cu_k;   // key prefix sums (chunked prefill), or nullptr: keys = queries
   const uint64_t* words;
   void* out;
+  float* lse;            // optional [N][Hq] log-sum-exp of each query row's scores
   const WorkItem* items;
   int32_t batch, max_seqlen, Hq, Hk, D, g, blk_q, T, G, nch, hc, nbq;
+  int32_t Tk;            // key tiles (T in prefill)
   float sm_log2;     // fl32(sm_scale * log2(e))
   int32_t out_fp32;
   int32_t kv_int8;
@@ -70,6 +82,7 @@ struct AttnArgs {
 
 struct SchedArgs {
   const int32_t* cu;
+  const int32_t* cu_k;  // key prefix sums (chunked prefill), or nullptr
   int32_t batch, T, Hk, nch;
   int32_t cost_shift;   // group costs >> cost_shift keep every XCD load below 2^28
   int64_t nslots, segmax;

@@ -12,7 +12,8 @@
 // items to one XCD where possible, so the K/V of a group is fetched from HBM
 // once into that XCD's L2 and reused by all of its query-tile rows:
 //   * groups are placed greedily, most expensive first (cost = sum over rows of
-//     the legal key tiles, T_b (T_b + 1) / 2 per head chunk), on the XCD with
+//     the legal key tiles, T_b (T_b + 1) / 2 per head chunk, plus T_b times the
+//     whole key tiles before the first query in chunked prefill), on the XCD with
 //     the least accumulated cost that still has free slots; a group that fits
 //     nowhere whole is split over the XCDs with the most free slots;
 //   * inside an XCD's list, groups follow each other and a group's items are in
@@ -85,7 +86,12 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
     const uint32_t tb = (uint32_t)uniform(tiles[b]);
     if (tb == 0) break;                           // sorted: the rest are empty too
     const uint32_t cnt = tb * (uint32_t)a.nch;
-    const uint32_t cost = (uint32_t)(((uint64_t)a.nch * tb * (tb + 1) / 2) >> a.cost_shift);
+    uint64_t tiles_b = (uint64_t)tb * (tb + 1) / 2;
+    if (a.cu_k) {                                 // chunked: queries start (Lk - Lq) keys in
+      const int lead = (uniform(a.cu_k[b + 1]) - uniform(a.cu_k[b])) - (uniform(a.cu[b + 1]) - uniform(a.cu[b]));
+      tiles_b += (uint64_t)tb * (uint32_t)max(lead, 0) / kTile;
+    }
+    const uint32_t cost = (uint32_t)(((uint64_t)a.nch * tiles_b) >> a.cost_shift);
     for (int hk = 0; hk < a.Hk; ++hk) {
       uint32_t remaining = cnt, ib = 0;
       while (remaining > 0 && nseg < segmax) {

@@ -49,14 +49,20 @@ int32_t check_common(int32_t batch, int32_t max_seqlen, const int32_t* cu) {
   return TILEMIX_OK;
 }
 
-int32_t check_groups(int32_t max_seqlen, int32_t g) {
+// Route groups of one row: the key tiles of max_seqlen_k (chunked) or of max_seqlen.
+int32_t check_groups(int32_t max_seqlen_keys, int32_t g) {
   if (g < 1) return fail(TILEMIX_ERR_INVALID_ARG, "g = %d must be >= 1", g);
-  const int64_t T = cdiv(max_seqlen, kTile);
+  const int64_t T = cdiv(max_seqlen_keys, kTile);
   if (cdiv(T, g) > 64)
     return fail(TILEMIX_ERR_TOO_MANY_GROUPS, "ceil(T/g) = %lld groups (T = %lld, g = %d) exceed one 64-bit word",
                 (long long)cdiv(T, g), (long long)T, g);
   return TILEMIX_OK;
 }
+
+// Query heads per workgroup at most: 3 with fp16 K/V; 2 with the INT8 KV cache,
+// whose register staging of the next tile leaves too few VGPRs for 3 (spills in
+// the inner loop cost more than loading each K/V tile once more).
+int32_t max_heads_per_chunk(const tilemix_attn_params* p) { return p->kv_int8 ? 2 : 3; }
 
 int32_t validate_attn_params(const tilemix_attn_params* p) {
   if (!p) return fail(TILEMIX_ERR_INVALID_ARG, "params is NULL");
@@ -78,13 +84,17 @@ int32_t validate_attn_params(const tilemix_attn_params* p) {
   if (p->otf_quant != 0 && p->otf_quant != 1) return fail(TILEMIX_ERR_INVALID_ARG, "otf_quant must be 0 or 1");
   if (p->otf_quant && p->kv_int8)
     return fail(TILEMIX_ERR_UNSUPPORTED, "otf_quant = 1 quantises an fp16 K: it cannot be combined with kv_int8 = 1");
+  if (p->max_seqlen_k < 0) return fail(TILEMIX_ERR_INVALID_ARG, "max_seqlen_k %d must be >= 0", p->max_seqlen_k);
+  if (p->max_seqlen_k > 0 && p->max_seqlen_k < p->max_seqlen)
+    return fail(TILEMIX_ERR_INVALID_ARG, "max_seqlen_k %d < max_seqlen %d: a chunk has no more queries than keys",
+                p->max_seqlen_k, p->max_seqlen);
   if (!(p->sm_scale > 0.0f) || !std::isfinite(p->sm_scale))
     return fail(TILEMIX_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
-  int32_t st = check_groups(p->max_seqlen, p->g);
+  int32_t st = check_groups(p->max_seqlen_k > 0 ? p->max_seqlen_k : p->max_seqlen, p->g);
   if (st != TILEMIX_OK) return st;
   // one workgroup per work item: the grid (256 threads each) must stay below 2^32 threads
   const int64_t items = (int64_t)p->batch * cdiv(p->max_seqlen, kTile) * p->num_kv_heads *
-                        cdiv(p->num_q_heads / p->num_kv_heads, 3);
+                        cdiv(p->num_q_heads / p->num_kv_heads, max_heads_per_chunk(p));
   if (items > (int64_t)1 << 24)
     return fail(TILEMIX_ERR_UNSUPPORTED, "%lld work items exceed one launch (2^24); split the batch",
                 (long long)items);
@@ -92,15 +102,16 @@ int32_t validate_attn_params(const tilemix_attn_params* p) {
 }
 
 struct Derived {
-  int32_t T, G, nch, hc, nbq;
+  int32_t T, Tk, G, nch, hc, nbq;   // T query tiles, Tk key tiles
   WorkspaceLayout ws;
 };
 
 Derived derive(const tilemix_attn_params* p) {
   Derived d;
   d.T = (int32_t)cdiv(p->max_seqlen, kTile);
+  d.Tk = (int32_t)cdiv(p->max_seqlen_k > 0 ? p->max_seqlen_k : p->max_seqlen, kTile);
   d.G = p->num_q_heads / p->num_kv_heads;
-  d.nch = (int32_t)cdiv(d.G, 3);          // at most 3 query heads per workgroup
+  d.nch = (int32_t)cdiv(d.G, max_heads_per_chunk(p));
   d.hc = (int32_t)cdiv(d.G, d.nch);       // heads per chunk (balanced)
   d.nbq = (int32_t)cdiv(p->max_seqlen, p->blk_q);
   d.ws = workspace_layout(p->batch, d.T, p->num_kv_heads, d.nch);
@@ -118,6 +129,10 @@ int32_t validate_tensors(const tilemix_attn_params* p, const tilemix_attn_tensor
   if (p->kv_int8 && !t->v_scale) return fail(TILEMIX_ERR_INVALID_ARG, "v_scale must be non-NULL when kv_int8 = 1");
   if (!t->cu_seqlens || !t->route_words || !t->out)
     return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens, route_words and out must be non-NULL");
+  if ((p->max_seqlen_k > 0) != (t->cu_seqlens_k != nullptr))
+    return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens_k must be given exactly when max_seqlen_k > 0 (chunked prefill)");
+  if ((t->cu_seqlens_k && !aligned(t->cu_seqlens_k, 4)) || (t->lse && !aligned(t->lse, 4)))
+    return fail(TILEMIX_ERR_INVALID_ARG, "misaligned cu_seqlens_k or lse pointer");
   if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16) || (!otf && !aligned(t->q_q, 16)) ||
       (!otf && t->k_q && !aligned(t->k_q, 16)) || !aligned(t->out, 16))
     return fail(TILEMIX_ERR_INVALID_ARG, "q, k, v, q_q, k_q and out must be 16-byte aligned");
@@ -137,15 +152,21 @@ int32_t validate_tensors(const tilemix_attn_params* p, const tilemix_attn_tensor
 enum class Mode { kPlanAndRun, kPlanOnly, kRunOnly };
 
 int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t, const int32_t* cu_seqlens,
-                    void* workspace, size_t workspace_bytes, const tilemix_debug* dbg, hipStream_t stream, Mode mode) {
+                    const int32_t* cu_seqlens_k, void* workspace, size_t workspace_bytes, const tilemix_debug* dbg,
+                    hipStream_t stream, Mode mode) {
   int32_t st = validate_attn_params(p);
   if (st != TILEMIX_OK) return st;
   if (mode != Mode::kPlanOnly) {
     st = validate_tensors(p, t);
     if (st != TILEMIX_OK) return st;
     cu_seqlens = t->cu_seqlens;
-  } else if (!cu_seqlens || !aligned(cu_seqlens, 4)) {
-    return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens must be a non-NULL, 4-byte aligned device pointer");
+    cu_seqlens_k = t->cu_seqlens_k;
+  } else {
+    if (!cu_seqlens || !aligned(cu_seqlens, 4))
+      return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens must be a non-NULL, 4-byte aligned device pointer");
+    if ((p->max_seqlen_k > 0) != (cu_seqlens_k != nullptr) || (cu_seqlens_k && !aligned(cu_seqlens_k, 4)))
+      return fail(TILEMIX_ERR_INVALID_ARG,
+                  "cu_seqlens_k must be a 4-byte aligned device pointer exactly when max_seqlen_k > 0");
   }
   const Derived d = derive(p);
   if (!workspace || workspace_bytes < d.ws.total)
@@ -165,13 +186,16 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
   char* ws = static_cast<char*>(workspace);
   SchedArgs sa;
   sa.cu = cu_seqlens;
+  sa.cu_k = cu_seqlens_k;
   sa.batch = p->batch;
   sa.T = d.T;
   sa.Hk = p->num_kv_heads;
   sa.nch = d.nch;
   {
-    // upper bound of the summed cost of all groups: every sequence at T tiles
-    const uint64_t total = (uint64_t)p->batch * p->num_kv_heads * d.nch * (uint64_t)d.T * (d.T + 1) / 2;
+    // upper bound of the summed cost of all groups: every sequence at T query
+    // tiles, each also behind up to Tk key tiles of earlier keys (chunked)
+    const uint64_t rows = (uint64_t)p->batch * p->num_kv_heads * d.nch * (uint64_t)d.T;
+    const uint64_t total = rows * (d.T + 1) / 2 + (p->max_seqlen_k > 0 ? rows * (uint64_t)d.Tk : 0);
     int shift = 0;
     while ((total >> shift) >= ((uint64_t)1 << 28)) ++shift;
     sa.cost_shift = shift;
@@ -203,8 +227,10 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
   a.k_scale = t->k_scale;
   a.v_scale = t->v_scale;
   a.cu = t->cu_seqlens;
+  a.cu_k = t->cu_seqlens_k;
   a.words = t->route_words;
   a.out = t->out;
+  a.lse = t->lse;
   a.items = sa.items;
   a.batch = p->batch;
   a.max_seqlen = p->max_seqlen;
@@ -214,6 +240,7 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
   a.g = p->g;
   a.blk_q = p->blk_q;
   a.T = d.T;
+  a.Tk = d.Tk;
   a.G = d.G;
   a.nch = d.nch;
   a.hc = d.hc;
@@ -230,7 +257,7 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
   }
   a.dbg_seq = -1;
   if (dbg) {
-    const int64_t tiles = (int64_t)p->batch * p->num_q_heads * d.T * d.T;
+    const int64_t tiles = (int64_t)p->batch * p->num_q_heads * d.T * d.Tk;
     if (dbg->visit_count) {
       e = launch_fill_u32(dbg->visit_count, 0u, tiles, stream);
       if (e != hipSuccess) return hip_status(e, "debug fill");
@@ -241,7 +268,7 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
     }
     if (dbg->s32_tiles) {
       e = launch_fill_u32(reinterpret_cast<uint32_t*>(dbg->s32_tiles), 0x80000000u,
-                          (int64_t)(dbg->m_end - dbg->m_begin) * d.T * kTile * kTile, stream);
+                          (int64_t)(dbg->m_end - dbg->m_begin) * d.Tk * kTile * kTile, stream);
       if (e != hipSuccess) return hip_status(e, "debug fill");
     }
     a.dbg_seq = dbg->s32_tiles ? dbg->seq : -1;
@@ -336,44 +363,56 @@ int32_t tilemix_quantize_blockwise(const void* x, int64_t stride_tok, int64_t st
   return hip_status(launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
-int32_t tilemix_build_route_mask(const uint8_t* tile_route, const int32_t* cu_seqlens, int32_t batch,
-                                 int32_t max_seqlen, int32_t num_kv_heads, int32_t g, uint64_t* route_words,
-                                 void* stream) {
-  int32_t st = check_common(batch, max_seqlen, cu_seqlens);
+static int32_t check_route_args(int32_t batch, int32_t max_seqlen, const int32_t* cu, const int32_t* cu_k,
+                         int32_t max_seqlen_k, int32_t num_kv_heads, int32_t g) {
+  int32_t st = check_common(batch, max_seqlen, cu);
   if (st != TILEMIX_OK) return st;
-  if (!tile_route || !route_words) return fail(TILEMIX_ERR_INVALID_ARG, "tile_route and route_words must be non-NULL");
   if (num_kv_heads < 1) return fail(TILEMIX_ERR_INVALID_ARG, "num_kv_heads %d must be >= 1", num_kv_heads);
+  if ((cu_k != nullptr) != (max_seqlen_k > 0))
+    return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens_k must be given exactly when max_seqlen_k > 0 (chunked prefill)");
+  if (max_seqlen_k < 0 || (max_seqlen_k > 0 && max_seqlen_k < max_seqlen))
+    return fail(TILEMIX_ERR_INVALID_ARG, "max_seqlen_k %d must be 0 or >= max_seqlen %d", max_seqlen_k, max_seqlen);
+  if (cu_k && !aligned(cu_k, 4)) return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens_k must be 4-byte aligned");
+  return check_groups(max_seqlen_k > 0 ? max_seqlen_k : max_seqlen, g);
+}
+
+int32_t tilemix_build_route_mask(const uint8_t* tile_route, const int32_t* cu_seqlens, const int32_t* cu_seqlens_k,
+                                 int32_t batch, int32_t max_seqlen, int32_t max_seqlen_k, int32_t num_kv_heads,
+                                 int32_t g, uint64_t* route_words, void* stream) {
+  if (!tile_route || !route_words) return fail(TILEMIX_ERR_INVALID_ARG, "tile_route and route_words must be non-NULL");
   if (!aligned(route_words, 8)) return fail(TILEMIX_ERR_INVALID_ARG, "route_words must be 8-byte aligned");
-  st = check_groups(max_seqlen, g);
+  int32_t st = check_route_args(batch, max_seqlen, cu_seqlens, cu_seqlens_k, max_seqlen_k, num_kv_heads, g);
   if (st != TILEMIX_OK) return st;
   RouteArgs a{};
   a.tile_route = tile_route;
   a.words_out = route_words;
   a.cu = cu_seqlens;
+  a.cu_k = cu_seqlens_k;
   a.batch = batch;
   a.T = (int32_t)cdiv(max_seqlen, kTile);
+  a.Tk = (int32_t)cdiv(max_seqlen_k > 0 ? max_seqlen_k : max_seqlen, kTile);
   a.num_kv_heads = num_kv_heads;
   a.g = g;
   return hip_status(launch_build_route(a, static_cast<hipStream_t>(stream)), "route-mask launch");
 }
 
-int32_t tilemix_decode_route_mask(const uint64_t* route_words, const int32_t* cu_seqlens, int32_t batch,
-                                  int32_t max_seqlen, int32_t num_kv_heads, int32_t g, uint8_t* tile_route_out,
+int32_t tilemix_decode_route_mask(const uint64_t* route_words, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen,
+                                  int32_t max_seqlen_k, int32_t num_kv_heads, int32_t g, uint8_t* tile_route_out,
                                   void* stream) {
-  int32_t st = check_common(batch, max_seqlen, cu_seqlens);
-  if (st != TILEMIX_OK) return st;
   if (!route_words || !tile_route_out)
     return fail(TILEMIX_ERR_INVALID_ARG, "route_words and tile_route_out must be non-NULL");
-  if (num_kv_heads < 1) return fail(TILEMIX_ERR_INVALID_ARG, "num_kv_heads %d must be >= 1", num_kv_heads);
   if (!aligned(route_words, 8)) return fail(TILEMIX_ERR_INVALID_ARG, "route_words must be 8-byte aligned");
-  st = check_groups(max_seqlen, g);
+  int32_t st = check_route_args(batch, max_seqlen, cu_seqlens, cu_seqlens_k, max_seqlen_k, num_kv_heads, g);
   if (st != TILEMIX_OK) return st;
   RouteArgs a{};
   a.words_in = route_words;
   a.tile_route_out = tile_route_out;
   a.cu = cu_seqlens;
+  a.cu_k = cu_seqlens_k;
   a.batch = batch;
   a.T = (int32_t)cdiv(max_seqlen, kTile);
+  a.Tk = (int32_t)cdiv(max_seqlen_k > 0 ? max_seqlen_k : max_seqlen, kTile);
   a.num_kv_heads = num_kv_heads;
   a.g = g;
   return hip_status(launch_decode_route(a, static_cast<hipStream_t>(stream)), "route-decode launch");
@@ -389,27 +428,27 @@ int32_t tilemix_attn_workspace_size(const tilemix_attn_params* params, size_t* b
 
 int32_t tilemix_attn_prefill(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  return attn_common(params, tensors, nullptr, workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream),
-                     Mode::kPlanAndRun);
+  return attn_common(params, tensors, nullptr, nullptr, workspace, workspace_bytes, nullptr,
+                     static_cast<hipStream_t>(stream), Mode::kPlanAndRun);
 }
 
-int32_t tilemix_attn_plan(const tilemix_attn_params* params, const int32_t* cu_seqlens, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  return attn_common(params, nullptr, cu_seqlens, workspace, workspace_bytes, nullptr,
+int32_t tilemix_attn_plan(const tilemix_attn_params* params, const int32_t* cu_seqlens, const int32_t* cu_seqlens_k,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_common(params, nullptr, cu_seqlens, cu_seqlens_k, workspace, workspace_bytes, nullptr,
                      static_cast<hipStream_t>(stream), Mode::kPlanOnly);
 }
 
 int32_t tilemix_attn_run(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return attn_common(params, tensors, nullptr, workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream),
-                     Mode::kRunOnly);
+  return attn_common(params, tensors, nullptr, nullptr, workspace, workspace_bytes, nullptr,
+                     static_cast<hipStream_t>(stream), Mode::kRunOnly);
 }
 
 int32_t tilemix_attn_prefill_debug(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors,
                                    void* workspace, size_t workspace_bytes, const tilemix_debug* dbg, void* stream) {
   if (!dbg) return fail(TILEMIX_ERR_INVALID_ARG, "dbg is NULL");
-  return attn_common(params, tensors, nullptr, workspace, workspace_bytes, dbg, static_cast<hipStream_t>(stream),
-                     Mode::kPlanAndRun);
+  return attn_common(params, tensors, nullptr, nullptr, workspace, workspace_bytes, dbg,
+                     static_cast<hipStream_t>(stream), Mode::kPlanAndRun);
 }
 
 }  // extern "C"

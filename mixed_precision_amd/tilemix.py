@@ -40,7 +40,8 @@ class AttnParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_seqlen", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("g", ctypes.c_int32),
                 ("blk_q", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("kv_int8", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("otf_quant", ctypes.c_int32)]
+                ("kv_int8", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("otf_quant", ctypes.c_int32),
+                ("max_seqlen_k", ctypes.c_int32)]
 
 
 class AttnTensors(ctypes.Structure):
@@ -49,7 +50,8 @@ class AttnTensors(ctypes.Structure):
                 ("kv_stride_tok", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
                 ("q_q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k_q", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
-                ("route_words", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+                ("route_words", ctypes.c_void_p), ("out", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p)]
 
 
 class Debug(ctypes.Structure):
@@ -72,15 +74,15 @@ def _load():
     lib.tilemix_quantize_blockwise.restype = i32
     lib.tilemix_quantize_blockwise.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.tilemix_build_route_mask.restype = i32
-    lib.tilemix_build_route_mask.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.tilemix_build_route_mask.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.tilemix_decode_route_mask.restype = i32
-    lib.tilemix_decode_route_mask.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.tilemix_decode_route_mask.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.tilemix_attn_workspace_size.restype = i32
     lib.tilemix_attn_workspace_size.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(sz)]
     lib.tilemix_attn_prefill.restype = i32
     lib.tilemix_attn_prefill.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(AttnTensors), vp, sz, vp]
     lib.tilemix_attn_plan.restype = i32
-    lib.tilemix_attn_plan.argtypes = [ctypes.POINTER(AttnParams), vp, vp, sz, vp]
+    lib.tilemix_attn_plan.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, sz, vp]
     lib.tilemix_attn_run.restype = i32
     lib.tilemix_attn_run.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(AttnTensors), vp, sz, vp]
     lib.tilemix_attn_prefill_debug.restype = i32
@@ -154,23 +156,30 @@ def tilemix_quantize_blockwise(x: torch.Tensor, cu_seqlens: torch.Tensor, max_se
 # ----------------------------------------------------------------------------- route words
 
 def tilemix_build_route_mask(tile_route: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, g: int,
-                             route_words: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """tile_route: uint8 [Hk][B][T][T].  Returns route words as int64 [Hk][B][T] (uint64 bit patterns)."""
+                             route_words: Optional[torch.Tensor] = None, stream=None,
+                             cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_k: int = 0) -> torch.Tensor:
+    """tile_route: uint8 [Hk][B][T][Tk].  Returns route words as int64 [Hk][B][T] (uint64 bit patterns).
+    cu_seqlens_k / max_seqlen_k: key prefix sums and bound for chunked prefill (None / 0: prefill)."""
     _expect(tile_route, torch.uint8, "tile_route")
     Hk, B, T, _ = tile_route.shape
     if route_words is None:
         route_words = torch.empty((Hk, B, T), dtype=torch.int64, device=tile_route.device)
-    _check(_lib.tilemix_build_route_mask(_ptr(tile_route.contiguous()), _ptr(cu_seqlens), B, int(max_seqlen), Hk,
-                                         int(g), _ptr(route_words), _stream(stream)))
+    _check(_lib.tilemix_build_route_mask(_ptr(tile_route.contiguous()), _ptr(cu_seqlens), _ptr(cu_seqlens_k), B,
+                                         int(max_seqlen), int(max_seqlen_k), Hk, int(g), _ptr(route_words),
+                                         _stream(stream)))
     return route_words
 
 
 def tilemix_decode_route_mask(route_words: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, g: int,
-                              stream=None) -> torch.Tensor:
+                              stream=None, cu_seqlens_k: Optional[torch.Tensor] = None,
+                              max_seqlen_k: int = 0) -> torch.Tensor:
+    """Returns uint8 [Hk][B][T][Tk]: the decoded bit of every legal tile, 0xFF elsewhere."""
     Hk, B, T = route_words.shape
-    out = torch.empty((Hk, B, T, T), dtype=torch.uint8, device=route_words.device)
-    _check(_lib.tilemix_decode_route_mask(_ptr(route_words), _ptr(cu_seqlens), B, int(max_seqlen), Hk, int(g),
-                                          _ptr(out), _stream(stream)))
+    Tk = num_tiles(max_seqlen_k if max_seqlen_k else max_seqlen)
+    out = torch.empty((Hk, B, T, Tk), dtype=torch.uint8, device=route_words.device)
+    _check(_lib.tilemix_decode_route_mask(_ptr(route_words), _ptr(cu_seqlens), _ptr(cu_seqlens_k), B,
+                                          int(max_seqlen), int(max_seqlen_k), Hk, int(g), _ptr(out),
+                                          _stream(stream)))
     return out
 
 
@@ -189,11 +198,12 @@ class AttnProblem:
     kv_int8: bool = False
     out_fp32: bool = False
     otf_quant: bool = False   # Q/K INT8 operands made inside the kernel (q_q, q_scale, k_q, k_scale unused)
+    max_seqlen_k: int = 0     # chunked prefill: bound of the key counts (0: prefill)
 
     def params(self) -> AttnParams:
         return AttnParams(self.batch, self.max_seqlen, self.num_q_heads, self.num_kv_heads, self.head_dim, self.g,
                           self.blk_q, float(self.sm_scale), 1, int(self.kv_int8), int(self.out_fp32),
-                          int(self.otf_quant))
+                          int(self.otf_quant), int(self.max_seqlen_k))
 
 
 def tilemix_attn_workspace_size(problem: AttnProblem) -> int:
@@ -203,7 +213,8 @@ def tilemix_attn_workspace_size(problem: AttnProblem) -> int:
     return int(n.value)
 
 
-def _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out) -> AttnTensors:
+def _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out, cu_seqlens_k=None,
+             lse=None) -> AttnTensors:
     if q.stride(2) != 1 or k.stride(2) != 1 or v.stride(2) != 1 or k.stride() != v.stride():
         raise ValueError("q/k/v channels must be contiguous and k, v must share strides")
     def st(t, dim):   # the stride of a size-1 dimension never addresses anything (it can be 0 on views)
@@ -214,7 +225,7 @@ def _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_wor
         return None if t is None else t.data_ptr()
     return AttnTensors(q.data_ptr(), k.data_ptr(), v.data_ptr(), st(q, 0), st(q, 1), st(k, 0), st(k, 1),
                        p(q_q), p(q_scale), p(k_q), p(k_scale), p(v_scale), cu_seqlens.data_ptr(),
-                       route_words.data_ptr(), out.data_ptr())
+                       route_words.data_ptr(), out.data_ptr(), p(cu_seqlens_k), p(lse))
 
 
 class AttnPlan:
@@ -226,23 +237,23 @@ class AttnPlan:
         self.ws_bytes = tilemix_attn_workspace_size(problem)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
 
-    def schedule(self, cu_seqlens, stream=None):
-        """tilemix_attn_plan: build the work list for `cu_seqlens` into the workspace."""
-        _check(_lib.tilemix_attn_plan(ctypes.byref(self.params), _ptr(cu_seqlens), _ptr(self.workspace),
-                                      self.ws_bytes, _stream(stream)))
+    def schedule(self, cu_seqlens, stream=None, cu_seqlens_k=None):
+        """tilemix_attn_plan: build the work list for `cu_seqlens` (and `cu_seqlens_k`) into the workspace."""
+        _check(_lib.tilemix_attn_plan(ctypes.byref(self.params), _ptr(cu_seqlens), _ptr(cu_seqlens_k),
+                                      _ptr(self.workspace), self.ws_bytes, _stream(stream)))
 
     def run_planned(self, q, k, v, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, out, v_scale=None,
-                    stream=None):
+                    stream=None, cu_seqlens_k=None, lse=None):
         """tilemix_attn_run: attention over the work list a previous schedule() built."""
-        t = _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out)
+        t = _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out, cu_seqlens_k, lse)
         _check(_lib.tilemix_attn_run(ctypes.byref(self.params), ctypes.byref(t), _ptr(self.workspace),
                                      self.ws_bytes, _stream(stream)))
         return out
 
     def run(self, q, k, v, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, out, v_scale=None,
-            debug: Optional[Debug] = None, stream=None):
+            debug: Optional[Debug] = None, stream=None, cu_seqlens_k=None, lse=None):
         """tilemix_attn_prefill (work list + attention), or its debug variant."""
-        t = _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out)
+        t = _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out, cu_seqlens_k, lse)
         if debug is None:
             st = _lib.tilemix_attn_prefill(ctypes.byref(self.params), ctypes.byref(t), _ptr(self.workspace),
                                            self.ws_bytes, _stream(stream))
@@ -256,11 +267,14 @@ class AttnPlan:
 def tilemix_attn_prefill(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g: int, q_q=None, q_scale=None,
                          k_q=None, k_scale=None, blk_q: int = 64, sm_scale: Optional[float] = None,
                          kv_int8: bool = False, v_scale=None, out_fp32: bool = False, otf_quant: bool = False,
-                         out=None, plan: Optional[AttnPlan] = None, stream=None) -> torch.Tensor:
-    """Fused routed causal prefill attention; returns out [N][Hq][d] (fp16, or fp32 if out_fp32).
+                         cu_seqlens_k=None, max_seqlen_k: int = 0, lse=None, out=None,
+                         plan: Optional[AttnPlan] = None, stream=None) -> torch.Tensor:
+    """Fused routed causal attention; returns out [N][Hq][d] (fp16, or fp32 if out_fp32).
 
     otf_quant=False takes the quantise-once operands q_q, q_scale, k_q, k_scale (k_q unused with kv_int8);
-    otf_quant=True makes them inside the kernel and ignores those arguments."""
+    otf_quant=True makes them inside the kernel and ignores those arguments.  cu_seqlens_k / max_seqlen_k:
+    chunked prefill or decode (the queries are the last positions of each sequence's keys).  lse: optional
+    float32 [N][Hq] output of each row's log-sum-exp."""
     N, Hq, d = q.shape
     Hk = k.shape[1]
     B = cu_seqlens.numel() - 1
@@ -268,34 +282,37 @@ def tilemix_attn_prefill(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g
         sm_scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     if plan is None:
         plan = AttnPlan(AttnProblem(B, int(max_seqlen), Hq, Hk, d, int(g), int(blk_q), float(sm_scale),
-                                    bool(kv_int8), bool(out_fp32), bool(otf_quant)), device=q.device)
+                                    bool(kv_int8), bool(out_fp32), bool(otf_quant), int(max_seqlen_k)),
+                        device=q.device)
     if out is None:
         out = torch.empty((N, Hq, d), dtype=torch.float32 if out_fp32 else torch.float16, device=q.device)
     return plan.run(q, k, v, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, out, v_scale=v_scale,
-                    stream=stream)
+                    stream=stream, cu_seqlens_k=cu_seqlens_k, lse=lse)
 
 
 def tilemix_attn_prefill_debug(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g: int, q_q=None,
                                q_scale=None, k_q=None, k_scale=None, blk_q: int = 64,
                                sm_scale: Optional[float] = None, kv_int8: bool = False, v_scale=None,
-                               out_fp32: bool = True, otf_quant: bool = False, seq: int = 0, q_head: int = 0,
-                               m_begin: int = 0, m_end: Optional[int] = None, stream=None):
+                               out_fp32: bool = True, otf_quant: bool = False, cu_seqlens_k=None,
+                               max_seqlen_k: int = 0, seq: int = 0, q_head: int = 0, m_begin: int = 0,
+                               m_end: Optional[int] = None, stream=None):
     """As tilemix_attn_prefill, plus (s32_tiles, visit_count, route_used) debug products."""
     N, Hq, d = q.shape
     Hk = k.shape[1]
     B = cu_seqlens.numel() - 1
     T = num_tiles(max_seqlen)
+    Tk = num_tiles(max_seqlen_k if max_seqlen_k else max_seqlen)
     if m_end is None:
         m_end = T
     if sm_scale is None:
         sm_scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     plan = AttnPlan(AttnProblem(B, int(max_seqlen), Hq, Hk, d, int(g), int(blk_q), float(sm_scale), bool(kv_int8),
-                                bool(out_fp32), bool(otf_quant)), device=q.device)
+                                bool(out_fp32), bool(otf_quant), int(max_seqlen_k)), device=q.device)
     out = torch.empty((N, Hq, d), dtype=torch.float32 if out_fp32 else torch.float16, device=q.device)
-    s32 = torch.empty((m_end - m_begin, T, TILE, TILE), dtype=torch.int32, device=q.device)
-    visits = torch.empty((B, Hq, T, T), dtype=torch.int32, device=q.device)
-    used = torch.empty((B, Hq, T, T), dtype=torch.uint8, device=q.device)
+    s32 = torch.empty((m_end - m_begin, Tk, TILE, TILE), dtype=torch.int32, device=q.device)
+    visits = torch.empty((B, Hq, T, Tk), dtype=torch.int32, device=q.device)
+    used = torch.empty((B, Hq, T, Tk), dtype=torch.uint8, device=q.device)
     dbg = Debug(seq, q_head, m_begin, m_end, s32.data_ptr(), visits.data_ptr(), used.data_ptr())
     plan.run(q, k, v, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, out, v_scale=v_scale, debug=dbg,
-             stream=stream)
+             stream=stream, cu_seqlens_k=cu_seqlens_k)
     return out, s32, visits, used

@@ -98,9 +98,12 @@ def test_null_pointer_and_workspace_errors(tm):
     assert lib.tilemix_attn_prefill_debug(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None,
                                           None) == 1
     # plan / run split: same validation, before any launch
-    assert lib.tilemix_attn_plan(ctypes.byref(p), None, ctypes.c_void_p(a), 1 << 30, None) == 1
-    assert lib.tilemix_attn_plan(ctypes.byref(p), ctypes.c_void_p(a), None, 0, None) == 4
-    assert lib.tilemix_attn_plan(ctypes.byref(pc), ctypes.c_void_p(a), ctypes.c_void_p(a), 1 << 30, None) == 2
+    assert lib.tilemix_attn_plan(ctypes.byref(p), None, None, ctypes.c_void_p(a), 1 << 30, None) == 1
+    assert lib.tilemix_attn_plan(ctypes.byref(p), ctypes.c_void_p(a), None, None, 0, None) == 4
+    assert lib.tilemix_attn_plan(ctypes.byref(pc), ctypes.c_void_p(a), None, ctypes.c_void_p(a), 1 << 30, None) == 2
+    # a plan with key prefix sums needs max_seqlen_k > 0, and the other way round
+    assert lib.tilemix_attn_plan(ctypes.byref(p), ctypes.c_void_p(a), ctypes.c_void_p(a), ctypes.c_void_p(a),
+                                 1 << 30, None) == 1
     assert lib.tilemix_attn_run(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 4
     t.q_stride_tok = 24 * 128 + 3
     assert lib.tilemix_attn_run(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 1
@@ -125,6 +128,35 @@ def test_on_the_fly_mode_validation(tm):
     assert e.value.status == 2 and "kv_int8" in str(e.value)
 
 
+def test_chunked_prefill_validation(tm):
+    """max_seqlen_k: >= 0, >= max_seqlen when set, its groups within one word;
+    cu_seqlens_k exactly when max_seqlen_k > 0; the workspace follows the query tiles."""
+    lib = tm.lib()
+    a = 1 << 20
+    with pytest.raises(tm.TilemixError) as e:
+        tm.tilemix_attn_workspace_size(_params(tm, max_seqlen_k=-1))
+    assert e.value.status == 1
+    with pytest.raises(tm.TilemixError) as e:
+        tm.tilemix_attn_workspace_size(_params(tm, max_seqlen=4096, max_seqlen_k=2048))
+    assert e.value.status == 1
+    with pytest.raises(tm.TilemixError) as e:
+        tm.tilemix_attn_workspace_size(_params(tm, max_seqlen=64, max_seqlen_k=64 * 65, g=1))
+    assert e.value.status == 3
+    n = tm.tilemix_attn_workspace_size(_params(tm, max_seqlen=64, max_seqlen_k=64 * 64, g=1))
+    assert n == tm.tilemix_attn_workspace_size(_params(tm, max_seqlen=64, g=1))
+    t = tm.AttnTensors(a, a, a, 24 * 128, 128, 8 * 128, 128, a, a, a, a, None, a, a, a)
+    pk = _params(tm, max_seqlen=64, max_seqlen_k=4096).params()
+    assert lib.tilemix_attn_prefill(ctypes.byref(pk), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 1
+    assert "cu_seqlens_k" in tm.last_error()
+    t.cu_seqlens_k = a
+    assert lib.tilemix_attn_prefill(ctypes.byref(pk), ctypes.byref(t), None, 0, None) == 4
+    p0 = _params(tm).params()
+    assert lib.tilemix_attn_prefill(ctypes.byref(p0), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 1
+    t.cu_seqlens_k = None
+    t.lse = a + 2
+    assert lib.tilemix_attn_prefill(ctypes.byref(p0), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 1
+
+
 def test_quantize_and_route_validation(tm):
     lib = tm.lib()
     a = ctypes.c_void_p(1 << 20)
@@ -133,8 +165,13 @@ def test_quantize_and_route_validation(tm):
     assert lib.tilemix_quantize_blockwise(a, 128, 128, a, 1, 64, 1, 128, 32, a, a, None) == 2
     assert lib.tilemix_quantize_blockwise(a, 129, 128, a, 1, 64, 1, 128, 64, a, a, None) == 1
     assert lib.tilemix_quantize_blockwise(a, 128, 128, None, 1, 64, 1, 128, 64, a, a, None) == 1
-    assert lib.tilemix_build_route_mask(a, a, 1, 64 * 65, 1, 1, a, None) == 3
-    assert lib.tilemix_build_route_mask(a, a, 1, 64 * 65, 1, 0, a, None) == 1
-    assert lib.tilemix_build_route_mask(None, a, 1, 64, 1, 1, a, None) == 1
-    assert lib.tilemix_decode_route_mask(a, a, 1, 64 * 129, 1, 2, a, None) == 3
+    assert lib.tilemix_build_route_mask(a, a, None, 1, 64 * 65, 0, 1, 1, a, None) == 3
+    assert lib.tilemix_build_route_mask(a, a, None, 1, 64 * 65, 0, 1, 0, a, None) == 1
+    assert lib.tilemix_build_route_mask(None, a, None, 1, 64, 0, 1, 1, a, None) == 1
+    assert lib.tilemix_decode_route_mask(a, a, None, 1, 64 * 129, 0, 1, 2, a, None) == 3
     assert "64-bit" in tm.last_error()
+    # chunked: the groups count key tiles (max_seqlen_k), and cu_seqlens_k goes with max_seqlen_k > 0
+    assert lib.tilemix_build_route_mask(a, a, a, 1, 64, 64 * 65, 1, 1, a, None) == 3
+    assert lib.tilemix_build_route_mask(a, a, a, 1, 64, 0, 1, 1, a, None) == 1
+    assert lib.tilemix_build_route_mask(a, a, None, 1, 64, 128, 1, 1, a, None) == 1
+    assert lib.tilemix_build_route_mask(a, a, a, 1, 128, 64, 1, 1, a, None) == 1

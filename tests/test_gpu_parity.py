@@ -3,7 +3,8 @@ same seeded inputs.
 
 Bars: bit-exact for the quantiser (int8 values and fp32 scales), the route
 words and their decode, the INT32 score tiles and the tile-visit counts;
-outputs (fp32 output option) within max-abs 2e-3 and relative Frobenius 1e-3.
+outputs (fp32 output option) within max-abs 2e-3 and relative Frobenius 1e-3;
+row log-sum-exp within 1e-3.
 """
 from __future__ import annotations
 
@@ -11,13 +12,16 @@ import numpy as np
 import pytest
 
 import oracle as orc
-from workloads import config, make_workload
+from workloads import config, make_workload, make_chunked_workload
 from tests.oracle_inputs import oracle_inputs
 
 pytestmark = pytest.mark.gpu
 
 MAX_ABS = 2e-3
 REL_FRO = 1e-3
+# log-sum-exp: the normaliser sums fp16-rounded probabilities (relative error
+# below 2^-11 for the sum) and v_log_f32 adds about 1 ulp, so |dLSE| < 1e-3
+LSE_ABS = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -130,6 +134,28 @@ def test_route_mask_bitexact(gp, g):
     ref = orc.build_route_mask(tr, w.cu_seqlens, w.max_seqlen, g)
     assert np.array_equal(gp.words_u64(words), ref)
     assert np.array_equal(dec.cpu().numpy(), orc.decode_route_mask(ref, w.cu_seqlens, w.max_seqlen, g))
+
+
+@pytest.mark.parametrize("g", [1, 3])
+def test_route_mask_chunked_bitexact(gp, g):
+    """Packer and decoder with key prefix sums (chunked prefill / decode): the
+    legal tiles of a row run to the key tile of its last query."""
+    import torch
+    _announce(f"route mask chunked g={g}")
+    Lq, Lk = [1, 70, 64, 200, 5], [1, 300, 64, 2600, 900]
+    w = make_chunked_workload(320 + g, lengths_q=Lq, lengths_k=Lk, num_q_heads=2, num_kv_heads=2, head_dim=64, g=1)
+    rng = np.random.default_rng(g)
+    tr = rng.integers(0, 3, size=(2, len(Lq), w.T, w.T_k)).astype(np.uint8)
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    cu_k = torch.from_numpy(w.cu_seqlens_k).cuda()
+    kw = dict(cu_seqlens_k=cu_k, max_seqlen_k=w.max_seqlen_k)
+    words = gp.tm.tilemix_build_route_mask(torch.from_numpy(tr).cuda(), cu, w.max_seqlen, g, **kw)
+    dec = gp.tm.tilemix_decode_route_mask(words, cu, w.max_seqlen, g, **kw)
+    torch.cuda.synchronize()
+    ref = orc.build_route_mask(tr, w.cu_seqlens, w.max_seqlen, g, w.cu_seqlens_k, w.max_seqlen_k)
+    assert np.array_equal(gp.words_u64(words), ref)
+    assert np.array_equal(dec.cpu().numpy(),
+                          orc.decode_route_mask(ref, w.cu_seqlens, w.max_seqlen, g, w.cu_seqlens_k, w.max_seqlen_k))
 
 
 def test_route_mask_too_many_groups(gp):
@@ -438,6 +464,104 @@ def test_deviation_sweep_matches_oracle(gp):
         assert abs(nh - no) <= 0.05 * no + 1e-5
         means[p] = nh
     assert means[1.0] > means[0.1] > 0
+
+
+# ------------------------------------------------------------------ chunked prefill / decode
+CHUNKED = [
+    # name, lengths_q, lengths_k, Hq, Hk, d, g, p, kv_int8, blk_q
+    ("chunk_gqa3_fp16kv", [200, 64, 1, 130], [1000, 64, 300, 1500], 6, 2, 128, 2, 0.5, False, 64),
+    ("chunk_int8kv_gqa7", [333, 50], [2000, 50], 7, 1, 128, 4, 0.6, True, 64),
+    ("chunk_d64_blkq128", [257, 100], [900, 700], 4, 2, 64, 1, 0.5, False, 128),
+    ("decode_int8kv", [1] * 37, [64 * 30 + 5 + 13 * i for i in range(37)], 4, 1, 128, 2, 0.5, True, 64),
+    ("decode_fp16kv_gqa4", [1] * 9, [1, 2, 63, 64, 65, 500, 1000, 2049, 4096], 8, 2, 128, 1, 0.7, False, 64),
+]
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=[c[0] for c in CHUNKED])
+def test_attn_chunked_full(gp, case):
+    """Chunked prefill and decode over a KV cache (bottom-right causal
+    alignment): output and log-sum-exp of every query against the oracle;
+    fp16-KV cases also through the on-the-fly mode (same bits)."""
+    import torch
+    name, Lq, Lk, hq, hk, d, g, p, kv8, blk_q = case
+    _announce(f"attn chunked {name}")
+    w = make_chunked_workload(500 + CHUNKED.index(case), lengths_q=Lq, lengths_k=Lk, num_q_heads=hq,
+                              num_kv_heads=hk, head_dim=d, g=g, p=p, outliers=True, kv_int8=kv8, blk_q=blk_q)
+    t = gp.prepare(w)
+    lse = torch.empty((w.q.shape[0], hq), dtype=torch.float32, device="cuda:0")
+    out = gp.attn(w, t, lse=lse)
+    otf = None if kv8 else gp.attn(w, t, otf=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.attn_prefill(oracle_inputs(w), with_lse=True)
+    ma, rf = gp.errors(out.cpu().numpy(), ref)
+    le = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse)))
+    print(f"  max_abs={ma:.3e} rel_fro={rf:.3e} lse_err={le:.3e}")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+    assert le <= LSE_ABS
+    if otf is not None:
+        assert torch.equal(otf, out)
+
+
+def test_attn_chunk_rows_equal_prefill_rows(gp):
+    """A chunk that starts on a Q block sees the same keys, scales and routes in
+    the same order as the same rows of the full prefill, so the HIP path gives
+    the same bits for them (and the same log-sum-exp)."""
+    import torch
+    _announce("attn chunk rows == prefill rows")
+    Lk = [1280, 700, 333]
+    Lq = [1280 - 1024, 700 - 512, 333]
+    full = make_workload(520, lengths=Lk, num_q_heads=6, num_kv_heads=2, head_dim=128, g=2, p=0.5, outliers=True)
+    chunk = make_chunked_workload(520, lengths_q=Lq, lengths_k=Lk, num_q_heads=6, num_kv_heads=2, head_dim=128,
+                                  g=2, p=0.5, outliers=True)
+    tf = gp.prepare(full)
+    lse_f = torch.empty((full.q.shape[0], 6), dtype=torch.float32, device="cuda:0")
+    of = gp.attn(full, tf, lse=lse_f)
+    tc = gp.prepare(chunk)
+    words = torch.zeros_like(tc["words"])
+    for b, (q_, k_) in enumerate(zip(Lq, Lk)):          # the chunk's rows of the full words
+        off = (k_ - q_) // 64
+        words[:, b, : (q_ + 63) // 64] = tf["words"][:, b, off: off + (q_ + 63) // 64]
+    tc["words"] = words
+    lse_c = torch.empty((chunk.q.shape[0], 6), dtype=torch.float32, device="cuda:0")
+    oc = gp.attn(chunk, tc, lse=lse_c)
+    torch.cuda.synchronize()
+    for b, (q_, k_) in enumerate(zip(Lq, Lk)):
+        s0q, s0k = int(chunk.cu_seqlens[b]), int(full.cu_seqlens[b])
+        assert torch.equal(oc[s0q:s0q + q_], of[s0k + k_ - q_:s0k + k_])
+        assert torch.equal(lse_c[s0q:s0q + q_], lse_f[s0k + k_ - q_:s0k + k_])
+
+
+def test_attn_chunked_debug_bitexact(gp):
+    """Chunked prefill: INT32 score tiles, visits and decoded routes bit-exact
+    (the causal edge cuts two key tiles for some query tiles)."""
+    import torch
+    _announce("attn chunked debug")
+    w = make_chunked_workload(530, lengths_q=[150, 40], lengths_k=[500, 40], num_q_heads=3, num_kv_heads=1,
+                              head_dim=128, g=1, p=0.6, outliers=True)
+    t = gp.prepare(w)
+    out, s32, visits, used = gp.attn_debug(w, t, seq=0, q_head=2)
+    torch.cuda.synchronize()
+    inp = oracle_inputs(w)
+    assert np.array_equal(s32.cpu().numpy(), orc.s32_tiles(inp, 0, 2, 0, w.T))
+    vis = orc.visit_matrix(w.cu_seqlens, w.max_seqlen, w.num_q_heads, w.cu_seqlens_k, w.max_seqlen_k)
+    assert np.array_equal(visits.cpu().numpy().astype(np.uint32), vis)
+    assert np.array_equal(used.cpu().numpy(), orc.route_used(inp))
+    ma, rf = gp.errors(out.cpu().numpy(), orc.attn_prefill(inp))
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+def test_attn_prefill_lse(gp):
+    """Prefill log-sum-exp of every query row against the oracle's."""
+    import torch
+    _announce("attn prefill lse")
+    w = make_workload(540, lengths=[300, 1, 129], num_q_heads=6, num_kv_heads=2, head_dim=128, g=1, p=0.5,
+                      outliers=True)
+    t = gp.prepare(w)
+    lse = torch.empty((w.q.shape[0], 6), dtype=torch.float32, device="cuda:0")
+    gp.attn(w, t, lse=lse)
+    torch.cuda.synchronize()
+    _, ref_lse = orc.attn_prefill(oracle_inputs(w), with_lse=True)
+    assert float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse))) <= LSE_ABS
 
 
 def _samples(w, rng, n):
