@@ -672,7 +672,13 @@ void attn_prefill_kernel(const AttnArgs a) {
     if (n + 2 > n_last) break;
   }
 
-  // ---- epilogue: O = acc / l
+  // ---- epilogue: O = acc / l.  Addresses are a wave-uniform base (the tile's
+  // first row, the chunk's first head) plus 32-bit per-lane offsets, so no
+  // 64-bit address stays live from the prologue.
+  const int64_t rowhead0 = ((int64_t)seq0 + m * kTile) * a.Hq + hk * a.G + h_begin;
+  float* lse_base = a.lse ? a.lse + rowhead0 : nullptr;
+  float* out32 = static_cast<float*>(a.out) + rowhead0 * D;
+  f16* out16 = static_cast<f16*>(a.out) + rowhead0 * D;
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     if (j >= nh) continue;
@@ -681,19 +687,20 @@ void attn_prefill_kernel(const AttnArgs a) {
     l += __shfl_xor(l, 32);
     const float inv = 1.0f / l;
     if (!qb_valid(j)) continue;
-    const int64_t tok = (int64_t)seq0 + m * kTile + qb_row(j);
+    // (row in tile) * Hq + (head in chunk)
+    const uint32_t e = (uint32_t)(qb_row(j) * a.Hq + ((wave * nh + j) >> 2));
     // log-sum-exp of the row's scores: the state is in log2 units of the
     // scaled scores, so LSE = (m_ref + log2 l) ln 2
-    if (a.lse && gq == 0) a.lse[tok * a.Hq + qb_head(j)] = (mref[j] + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
-    const int64_t base = (tok * a.Hq + qb_head(j)) * D;
+    if (lse_base && gq == 0) lse_base[e] = (mref[j] + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x4 r = O[j][db] * inv;
+      const uint32_t o = e * D + db * 16 + gq * 4;
       if (a.out_fp32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + base + db * 16 + gq * 4) = r;
+        *reinterpret_cast<f32x4*>(out32 + o) = r;
       } else {
         f16x4 hv = {(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
-        *reinterpret_cast<f16x4*>(static_cast<f16*>(a.out) + base + db * 16 + gq * 4) = hv;
+        *reinterpret_cast<f16x4*>(out16 + o) = hv;
       }
     }
   }
