@@ -317,8 +317,7 @@ struct Attn {
 #pragma unroll
       for (int j = 0; j < QB; ++j) {
         float mx = lm[j];
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16));
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+        mx = rows4_max(mx);
         const float tmax = mx * cj[j];
         const bool moved = tmax > mref[j] + kSlack;
         const float alpha = moved ? __builtin_amdgcn_exp2f(mref[j] - tmax) : 1.0f;
@@ -683,8 +682,7 @@ void attn_prefill_kernel(const AttnArgs a) {
   for (int j = 0; j < QB; ++j) {
     if (j >= nh) continue;
     float l = lrow[j];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = rows4_sum(l);
     const float inv = 1.0f / l;
     if (!qb_valid(j)) continue;
     // (row in tile) * Hq + (head in chunk)

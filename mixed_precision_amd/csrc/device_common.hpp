@@ -49,6 +49,39 @@ TM_DEV uint64_t uniform64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (one lane per 16-lane
+// row): gfx950's row-swapping permutes exchange rows 0<->1, 2<->3, then the two
+// halves of the wave, in registers with no LDS round trip.  With both operands
+// holding x, v_permlane16_swap leaves (x0 x0 x2 x2) in its first register and
+// (x1 x1 x3 x3) in its second (by 16-lane rows); v_permlane32_swap leaves
+// (x_lo x_lo) and (x_hi x_hi).  Combining the two registers after each swap
+// leaves every lane with (x0 op x1) op (x2 op x3).
+//
+// The swaps are written as asm: ROCm 7.2's builtins for them return the first
+// register twice.  The asm carries the wait states a permute needs after a
+// VALU write of its operands (the hazard recognizer does not look inside asm).
+TM_DEV void permlane16_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+TM_DEV void permlane32_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+template <typename Op>
+TM_DEV float rows4_reduce(float x, Op op) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane16_swap(a, b);
+  const float y = op(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  uint32_t c = __builtin_bit_cast(uint32_t, y), d = c;
+  permlane32_swap(c, d);
+  return op(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
+}
+TM_DEV float rows4_max(float x) {
+  return rows4_reduce(x, [](float u, float v) { return __builtin_elementwise_maximum(u, v); });
+}
+TM_DEV float rows4_sum(float x) {
+  return rows4_reduce(x, [](float u, float v) { return u + v; });
+}
+
 TM_DEV uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
