@@ -127,8 +127,8 @@ def deviation_sweep(args, w, plan, q, k, v, cu, q_q, q_s, k_q, k_s, v_q, v_s, wo
     import torch
     from mixed_precision_amd import tilemix as tm
     from workloads import route_bernoulli_groups
-    if args.config == 3:
-        raise SystemExit("--deviation-sweep needs a Bernoulli-routed workload (configs 1, 2, 4, 5)")
+    if args.config == 3 and not args.template:
+        raise SystemExit("--deviation-sweep needs a Bernoulli-routed workload (configs 1, 2, 4, 5) or --template")
     dev = q.device
     ps = [float(x) for x in args.deviation_sweep.split(",")]
     if 0.0 not in ps:
@@ -146,9 +146,13 @@ def deviation_sweep(args, w, plan, q, k, v, cu, q_q, q_s, k_q, k_s, v_q, v_s, wo
     ref = None
     outs = {}
     for p in sorted(set(ps)):
-        tr = torch.from_numpy(route_bernoulli_groups(w.cfg_id, w.num_kv_heads, [int(x) for x in w.lengths], w.T,
-                                                     w.g, p)).to(dev)
-        tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
+        if args.template:
+            tm.tilemix_template_route_words(args.template, int(round(p * 1000)), 2026, cu, w.max_seqlen,
+                                            w.num_kv_heads, w.g, route_words=words, stream=stream)
+        else:
+            tr = torch.from_numpy(route_bernoulli_groups(w.cfg_id, w.num_kv_heads, [int(x) for x in w.lengths],
+                                                         w.T, w.g, p)).to(dev)
+            tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
         work = work_model(w, words.cpu().numpy().view(np.uint64))
         out = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -162,7 +166,7 @@ def deviation_sweep(args, w, plan, q, k, v, cu, q_q, q_s, k_q, k_s, v_q, v_s, wo
         if ref is None:
             ref = out
         diff = (out - ref).abs()
-        res = {"deviation_sweep": w.name, "p": p, "int8_pair_fraction": work["pairs_int8"] / work["pairs"],
+        res = {"deviation_sweep": w.name, "routing": args.template or "bernoulli", "p": p, "int8_pair_fraction": work["pairs_int8"] / work["pairs"],
                "max_diff": float(diff.max()), "mean_diff": float(diff.double().mean()),
                "reference": "same inputs at 0 % INT8 (all tiles FP16)", "attn_ms_fp32_out": e0.elapsed_time(e1)}
         del diff
@@ -182,6 +186,9 @@ def main():
     ap.add_argument("--deviation-sweep", type=str, default=None, metavar="P,P,...",
                     help="instead of the bench line: MaxDiff / MeanDiff of the routed output against the "
                          "0 %% INT8 output at each INT8 coverage (Bernoulli-routed workloads), one JSON line each")
+    ap.add_argument("--template", type=str, default=None,
+                    help="with --deviation-sweep: route by a static template (band, global, row_random, "
+                         "aligned_sparse, bigbird, sptrans) instead of Bernoulli tile groups")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

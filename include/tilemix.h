@@ -125,6 +125,44 @@ int32_t tilemix_decode_route_mask(const uint64_t* route_words, const int32_t* cu
                                   int32_t max_seqlen_k, int32_t num_kv_heads, int32_t g,
                                   uint8_t* tile_route_out, void* stream);
 
+/* Static routing templates (see tilemix_template_route_words). */
+typedef enum {
+  TILEMIX_TEMPLATE_ALL_FP16 = 0,
+  TILEMIX_TEMPLATE_ALL_INT8 = 1,
+  TILEMIX_TEMPLATE_BAND = 2,
+  TILEMIX_TEMPLATE_GLOBAL = 3,
+  TILEMIX_TEMPLATE_ROW_RANDOM = 4,
+  TILEMIX_TEMPLATE_ALIGNED_SPARSE = 5,
+  TILEMIX_TEMPLATE_BIGBIRD = 6,
+  TILEMIX_TEMPLATE_SPTRANS = 7
+} tilemix_template;
+
+/*
+ * Route words of a static, data-free routing template at a target INT8 coverage
+ * of the legal tile groups ([PL App. B] names the layouts and the coverage
+ * settings; [PL Limitations] and [GS]: templates are built once and reused).
+ * The pages print no definitions; per query-tile row with n legal groups,
+ * F = (( 1000 - int8_permille) * n + 500) / 1000 groups stay FP16, the other legal
+ * groups are INT8:
+ *   BAND            the F groups nearest the diagonal
+ *   GLOBAL          the first F groups
+ *   ROW_RANDOM      the F groups with the smallest SplitMix64 keys of
+ *                   seed ^ (((hk * batch + b) * T + m) * 64 + j) (ties: lower j)
+ *   ALIGNED_SPARSE  the groups floor(k * n / F), k = 0 .. F-1
+ *   BIGBIRD         ceil(F/3) band groups, then ceil((F - that)/2) first groups,
+ *                   then random groups in key order up to F (an approximation)
+ *   SPTRANS         ceil(F/2) band groups, then F - ceil(F/2) groups evenly spaced
+ *                   before the band (local + strided; an approximation)
+ *   ALL_FP16 / ALL_INT8 ignore int8_permille.
+ * Chunked prefill: cu_seqlens_k / max_seqlen_k as for tilemix_build_route_mask.
+ *   route_words  uint64 [num_kv_heads][batch][T] (written), bits of illegal groups 0.
+ *   int8_permille 0 .. 1000; g >= 1 with ceil(Tk/g) <= 64.
+ */
+int32_t tilemix_template_route_words(int32_t template_kind, int32_t int8_permille, uint64_t seed,
+                                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_k, int32_t batch,
+                                     int32_t max_seqlen, int32_t max_seqlen_k, int32_t num_kv_heads,
+                                     int32_t g, uint64_t* route_words, void* stream);
+
 /* Host struct: problem description of one attention call. */
 typedef struct {
   int32_t batch;        /* sequences, >= 1 */

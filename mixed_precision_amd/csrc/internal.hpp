@@ -98,6 +98,7 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t T, int32_t Hk, int32_t n
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_build_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_template_route(const RouteArgs& a, int32_t kind, int32_t permille, uint64_t seed, hipStream_t s);
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t count, hipStream_t s);
 hipError_t launch_fill_u8(uint8_t* p, uint8_t value, int64_t count, hipStream_t s);

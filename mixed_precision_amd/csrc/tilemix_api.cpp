@@ -418,6 +418,31 @@ int32_t tilemix_decode_route_mask(const uint64_t* route_words, const int32_t* cu
   return hip_status(launch_decode_route(a, static_cast<hipStream_t>(stream)), "route-decode launch");
 }
 
+int32_t tilemix_template_route_words(int32_t template_kind, int32_t int8_permille, uint64_t seed,
+                                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_k, int32_t batch,
+                                     int32_t max_seqlen, int32_t max_seqlen_k, int32_t num_kv_heads,
+                                     int32_t g, uint64_t* route_words, void* stream) {
+  if (template_kind < TILEMIX_TEMPLATE_ALL_FP16 || template_kind > TILEMIX_TEMPLATE_SPTRANS)
+    return fail(TILEMIX_ERR_INVALID_ARG, "template kind %d unknown", template_kind);
+  if (int8_permille < 0 || int8_permille > 1000)
+    return fail(TILEMIX_ERR_INVALID_ARG, "int8_permille %d out of [0, 1000]", int8_permille);
+  if (!route_words) return fail(TILEMIX_ERR_INVALID_ARG, "route_words must be non-NULL");
+  if (!aligned(route_words, 8)) return fail(TILEMIX_ERR_INVALID_ARG, "route_words must be 8-byte aligned");
+  int32_t st = check_route_args(batch, max_seqlen, cu_seqlens, cu_seqlens_k, max_seqlen_k, num_kv_heads, g);
+  if (st != TILEMIX_OK) return st;
+  RouteArgs a{};
+  a.words_out = route_words;
+  a.cu = cu_seqlens;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.T = (int32_t)cdiv(max_seqlen, kTile);
+  a.Tk = (int32_t)cdiv(max_seqlen_k > 0 ? max_seqlen_k : max_seqlen, kTile);
+  a.num_kv_heads = num_kv_heads;
+  a.g = g;
+  return hip_status(launch_template_route(a, template_kind, int8_permille, seed, static_cast<hipStream_t>(stream)),
+                    "template launch");
+}
+
 int32_t tilemix_attn_workspace_size(const tilemix_attn_params* params, size_t* bytes) {
   if (!bytes) return fail(TILEMIX_ERR_INVALID_ARG, "bytes is NULL");
   int32_t st = validate_attn_params(params);

@@ -27,7 +27,12 @@ STATUS_NAMES = {0: "TILEMIX_OK", 1: "TILEMIX_ERR_INVALID_ARG", 2: "TILEMIX_ERR_U
 # Every symbol include/tilemix.h declares.
 EXPORTED = ("tilemix_status_string", "tilemix_last_error", "tilemix_version", "tilemix_quantize_blockwise",
             "tilemix_build_route_mask", "tilemix_decode_route_mask", "tilemix_attn_workspace_size",
-            "tilemix_attn_prefill", "tilemix_attn_plan", "tilemix_attn_run", "tilemix_attn_prefill_debug")
+            "tilemix_attn_prefill", "tilemix_attn_plan", "tilemix_attn_run", "tilemix_attn_prefill_debug",
+            "tilemix_template_route_words")
+
+# Static routing templates (tilemix_template enum of include/tilemix.h).
+TEMPLATES = {"all_fp16": 0, "all_int8": 1, "band": 2, "global": 3, "row_random": 4, "aligned_sparse": 5,
+             "bigbird": 6, "sptrans": 7}
 
 
 class TilemixError(RuntimeError):
@@ -77,6 +82,8 @@ def _load():
     lib.tilemix_build_route_mask.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.tilemix_decode_route_mask.restype = i32
     lib.tilemix_decode_route_mask.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.tilemix_template_route_words.restype = i32
+    lib.tilemix_template_route_words.argtypes = [i32, i32, ctypes.c_uint64, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.tilemix_attn_workspace_size.restype = i32
     lib.tilemix_attn_workspace_size.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(sz)]
     lib.tilemix_attn_prefill.restype = i32
@@ -181,6 +188,24 @@ def tilemix_decode_route_mask(route_words: torch.Tensor, cu_seqlens: torch.Tenso
                                           int(max_seqlen), int(max_seqlen_k), Hk, int(g), _ptr(out),
                                           _stream(stream)))
     return out
+
+
+def tilemix_template_route_words(kind: str, int8_permille: int, seed: int, cu_seqlens: torch.Tensor, max_seqlen: int,
+                                 num_kv_heads: int, g: int, cu_seqlens_k: Optional[torch.Tensor] = None,
+                                 max_seqlen_k: int = 0, route_words: Optional[torch.Tensor] = None,
+                                 stream=None) -> torch.Tensor:
+    """Route words int64 [Hk][B][T] of a static template ('band', 'global', 'row_random', 'aligned_sparse',
+    'bigbird', 'sptrans', 'all_fp16', 'all_int8') at int8_permille / 1000 INT8 coverage of the legal groups."""
+    _expect(cu_seqlens, torch.int32, "cu_seqlens")
+    B = cu_seqlens.numel() - 1
+    T = num_tiles(max_seqlen)
+    if route_words is None:
+        route_words = torch.empty((num_kv_heads, B, T), dtype=torch.int64, device=cu_seqlens.device)
+    _check(_lib.tilemix_template_route_words(TEMPLATES[kind], int(int8_permille), int(seed) & ((1 << 64) - 1),
+                                             _ptr(cu_seqlens), _ptr(cu_seqlens_k), B, int(max_seqlen),
+                                             int(max_seqlen_k), int(num_kv_heads), int(g), _ptr(route_words),
+                                             _stream(stream)))
+    return route_words
 
 
 # ----------------------------------------------------------------------------- attention

@@ -222,6 +222,103 @@ def decode_route_mask(words: np.ndarray, cu_seqlens, max_seqlen: int, g: int, cu
 
 
 # ---------------------------------------------------------------------------
+# Static routing templates [PL App. B], [PL Limitations], [GS]
+# ---------------------------------------------------------------------------
+# The pages list All-FP16, All-INT8, Band, Global, Row-Random, Aligned-Sparse,
+# BigBird and SpTrans layouts, built statically and data-free, at a target INT8
+# coverage of the legal tile groups, but print no definitions.  Readings taken
+# (all per query-tile row, over its legal groups j = 0 .. n-1 where n =
+# last_key_tile(m) // g + 1; F FP16 groups, F = round((1 - p) n) in exact
+# integer arithmetic with p in per mille; every other legal group is INT8):
+#   band:           the F groups nearest the diagonal (j >= n - F);
+#   global:         the first F groups (j < F);
+#   row_random:     the F groups with the smallest splitmix64 keys;
+#   aligned_sparse: F evenly spaced groups j = floor(k n / F), k = 0 .. F-1;
+#   bigbird:        ceil(F/3) band groups, then ceil((F - that)/2) first
+#                   groups, then random groups (key order) up to F in total;
+#   sptrans:        ceil(F/2) band groups, then the rest evenly spaced over
+#                   the groups before the band (local + strided).
+# BigBird and SpTrans are approximations of those papers' patterns at this
+# granularity.
+
+TEMPLATES = ("all_fp16", "all_int8", "band", "global", "row_random", "aligned_sparse", "bigbird", "sptrans")
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(x: int) -> int:
+    """SplitMix64 output function (Steele, Lea and Flood, 2014) of a 64-bit value."""
+    z = (x + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def template_key(seed: int, hk: int, b: int, m: int, j: int, batch: int, Tq: int) -> int:
+    """Random key of group j of row (hk, b, m): splitmix64 of seed XOR a unique counter."""
+    return splitmix64((int(seed) ^ ((((hk * batch + b) * Tq + m) * 64) + j)) & _M64)
+
+
+def fp16_groups(kind: str, n: int, permille: int, keys) -> set:
+    """The FP16 groups of one row with n legal groups (readings above)."""
+    if kind == "all_fp16":
+        return set(range(n))
+    if kind == "all_int8":
+        return set()
+    F = ((1000 - permille) * n + 500) // 1000
+    by_key = sorted(range(n), key=lambda j: (keys[j], j))
+    if kind == "band":
+        return set(range(n - F, n))
+    if kind == "global":
+        return set(range(F))
+    if kind == "row_random":
+        return set(by_key[:F])
+    if kind == "aligned_sparse":
+        return {k * n // F for k in range(F)}
+    if kind == "bigbird":
+        w = (F + 2) // 3
+        s = set(range(n - w, n))
+        s |= set(range((F - w + 1) // 2))
+        for j in by_key:
+            if len(s) >= F:
+                break
+            s.add(j)
+        return s
+    if kind == "sptrans":
+        w = (F + 1) // 2
+        k = F - w
+        s = set(range(n - w, n))
+        s |= {i * (n - w) // k for i in range(k)} if k else set()
+        return s
+    raise ValueError(kind)
+
+
+def template_route_words(kind: str, permille: int, seed: int, cu_seqlens, max_seqlen: int, num_kv_heads: int,
+                         g: int, cu_seqlens_k=None, max_seqlen_k: Optional[int] = None) -> np.ndarray:
+    """uint64 [Hk][B][Tq]: route words of a static template (bit j = 1: group j INT8)."""
+    if kind not in TEMPLATES or not 0 <= permille <= 1000:
+        raise ValueError("template")
+    pairs = _pairs(cu_seqlens, cu_seqlens_k)
+    Tq = num_tiles(max_seqlen)
+    Tk = num_tiles(max_seqlen if max_seqlen_k is None else max_seqlen_k)
+    if g < 1 or _cdiv(Tk, g) > 64:
+        raise ValueError("more than 64 route groups per row")
+    B = len(pairs)
+    words = np.zeros((num_kv_heads, B, Tq), dtype=np.uint64)
+    for hk in range(num_kv_heads):
+        for b, (Lq, Lk) in enumerate(pairs):
+            for m in range(num_tiles(Lq)):
+                n = last_key_tile(m, Lq, Lk) // g + 1
+                keys = [template_key(seed, hk, b, m, j, B, Tq) for j in range(n)]
+                f = fp16_groups(kind, n, permille, keys)
+                w = 0
+                for j in range(n):
+                    if j not in f:
+                        w |= 1 << j
+                words[hk, b, m] = np.uint64(w)
+    return words
+
+
+# ---------------------------------------------------------------------------
 # O4-O6. Routed scores, streaming online softmax, normalisation
 #        [PL §1; PL §3 Preliminaries; PL App. C; AN; GS]
 # ---------------------------------------------------------------------------

@@ -34,7 +34,8 @@ def test_header_declares_expected_calls():
     names = header_functions()
     for n in ("tilemix_quantize_blockwise", "tilemix_build_route_mask", "tilemix_decode_route_mask",
               "tilemix_attn_workspace_size", "tilemix_attn_prefill", "tilemix_attn_plan", "tilemix_attn_run",
-              "tilemix_attn_prefill_debug", "tilemix_status_string", "tilemix_last_error"):
+              "tilemix_attn_prefill_debug", "tilemix_status_string", "tilemix_last_error",
+              "tilemix_template_route_words"):
         assert n in names
 
 
@@ -155,6 +156,18 @@ def test_chunked_prefill_validation(tm):
     t.cu_seqlens_k = None
     t.lse = a + 2
     assert lib.tilemix_attn_prefill(ctypes.byref(p0), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 1
+
+
+def test_template_validation(tm):
+    lib = tm.lib()
+    a = ctypes.c_void_p(1 << 20)
+    assert lib.tilemix_template_route_words(8, 500, 1, a, None, 1, 64, 0, 1, 1, a, None) == 1
+    assert lib.tilemix_template_route_words(-1, 500, 1, a, None, 1, 64, 0, 1, 1, a, None) == 1
+    assert lib.tilemix_template_route_words(2, 1001, 1, a, None, 1, 64, 0, 1, 1, a, None) == 1
+    assert lib.tilemix_template_route_words(2, 500, 1, a, None, 1, 64 * 65, 0, 1, 1, a, None) == 3
+    assert lib.tilemix_template_route_words(2, 500, 1, a, None, 1, 64, 0, 1, 1, None, None) == 1
+    assert lib.tilemix_template_route_words(2, 500, 1, a, a, 1, 64, 0, 1, 1, a, None) == 1
+    assert tm.TEMPLATES["sptrans"] == 7
 
 
 def test_quantize_and_route_validation(tm):

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle as orc
-from workloads import config, make_workload, make_chunked_workload
+from workloads import config, make_workload, make_chunked_workload, cu_from_lengths
 from tests.oracle_inputs import oracle_inputs
 
 pytestmark = pytest.mark.gpu
@@ -156,6 +156,31 @@ def test_route_mask_chunked_bitexact(gp, g):
     assert np.array_equal(gp.words_u64(words), ref)
     assert np.array_equal(dec.cpu().numpy(),
                           orc.decode_route_mask(ref, w.cu_seqlens, w.max_seqlen, g, w.cu_seqlens_k, w.max_seqlen_k))
+
+
+@pytest.mark.parametrize("chunked", [False, True])
+def test_template_route_words_bitexact(gp, chunked):
+    """Static routing templates: every template, several coverages and group
+    sizes, prefill and chunked, bit-exact against the oracle's words."""
+    import torch
+    _announce(f"templates chunked={chunked}")
+    if chunked:
+        Lq, Lk = [300, 1, 64, 2000], [3000, 700, 64, 2000]
+    else:
+        Lq = Lk = [3000, 700, 64, 1, 4096]
+    cu_h, cuk_h = cu_from_lengths(Lq), cu_from_lengths(Lk)
+    cu = torch.from_numpy(cu_h).cuda()
+    cu_k = torch.from_numpy(cuk_h).cuda() if chunked else None
+    mq, mk = max(Lq), max(Lk)
+    for g in (1, 2):
+        for permille in (0, 50, 250, 500, 750, 1000, 333):
+            for kind in orc.TEMPLATES:
+                seed = 1234 + permille
+                got = gp.tm.tilemix_template_route_words(kind, permille, seed, cu, mq, 3, g, cu_seqlens_k=cu_k,
+                                                         max_seqlen_k=mk if chunked else 0)
+                ref = orc.template_route_words(kind, permille, seed, cu_h, mq, 3, g, cuk_h if chunked else None,
+                                               mk if chunked else None)
+                assert np.array_equal(gp.words_u64(got), ref), (kind, permille, g)
 
 
 def test_route_mask_too_many_groups(gp):

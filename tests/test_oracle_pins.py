@@ -365,6 +365,90 @@ def test_pin_M_chunked_legality_and_packer():
                 assert int(words[0, b, m]) == want
 
 
+# ---------------------------------------------------------------- pin N
+def test_pin_N_splitmix64_reference_outputs():
+    """The templates' counter-based generator against SplitMix64's published outputs."""
+    ref = json.load(open(os.path.join(GOLDEN, "splitmix64_seed0.json")))["outputs_hex"]
+    golden = 0x9E3779B97F4A7C15
+    got = [orc.splitmix64((k * golden) & ((1 << 64) - 1)) for k in range(3)]
+    assert got == [int(x, 16) for x in ref]
+
+
+@pytest.mark.parametrize("chunked", [False, True])
+def test_pin_N_template_coverage_and_structure(chunked):
+    """Static templates ([PL App. B]): in every row exactly F = round((1-p) n)
+    legal groups are FP16 (the rest INT8, nothing past the row's last legal
+    group), so the INT8 coverage of legal groups is within rounding of p; band
+    is the diagonal suffix, global the prefix, aligned-sparse evenly spaced,
+    SpTrans and BigBird contain their band (and BigBird its global) part; the
+    words survive a decode and re-pack unchanged."""
+    if chunked:
+        Lq, Lk, mq, mk = [300, 1, 64], [3000, 700, 64], 300, 3000
+        cu, cu_k = cu_from_lengths(Lq), cu_from_lengths(Lk)
+    else:
+        Lq = Lk = [3000, 700, 64]
+        mq = mk = 3000
+        cu, cu_k = cu_from_lengths(Lq), None
+    g = 1
+    for permille in (0, 250, 500, 750, 1000, 333):
+        for kind in orc.TEMPLATES:
+            w = orc.template_route_words(kind, permille, 11, cu, mq, 2, g, cu_k, None if cu_k is None else mk)
+            int8 = legal = 0
+            for hk in range(2):
+                for b in range(3):
+                    for m in range(orc.num_tiles(Lq[b])):
+                        n = orc.last_key_tile(m, Lq[b], Lk[b]) // g + 1
+                        word = int(w[hk, b, m])
+                        assert word >> n == 0
+                        fp = {j for j in range(n) if not (word >> j) & 1}
+                        F = ((1000 - permille) * n + 500) // 1000
+                        if kind == "all_fp16":
+                            assert len(fp) == n
+                        elif kind == "all_int8":
+                            assert not fp
+                        else:
+                            assert len(fp) == F, (kind, permille, n)
+                        if kind == "band":
+                            assert fp == set(range(n - F, n))
+                        if kind == "global":
+                            assert fp == set(range(F))
+                        if kind == "aligned_sparse" and F > 1:
+                            gaps = np.diff(sorted(fp))
+                            assert gaps.max() - gaps.min() <= 1
+                        if kind == "sptrans":
+                            assert set(range(n - (F + 1) // 2, n)) <= fp
+                        if kind == "bigbird":
+                            wb = (F + 2) // 3
+                            assert set(range(n - wb, n)) | set(range((F - wb + 1) // 2)) <= fp
+                        int8 += n - len(fp)
+                        legal += n
+            if kind not in ("all_fp16", "all_int8") and not chunked:
+                assert abs(int8 / legal - permille / 1000) < 0.02
+            # decode + AND re-pack gives the same words (the packer's legality agrees)
+            Tq, Tk = orc.num_tiles(mq), orc.num_tiles(mk)
+            dec = orc.decode_route_mask(w, cu, mq, g, cu_k, None if cu_k is None else mk)
+            tr = np.where(dec == 0xFF, 0, dec).astype(np.uint8)
+            assert np.array_equal(orc.build_route_mask(tr, cu, mq, g, cu_k, None if cu_k is None else mk), w)
+
+
+def test_pin_N_row_random_is_seeded_and_spread():
+    """Row-Random: deterministic per seed, different across seeds, and every
+    group position about equally likely to stay FP16."""
+    cu = cu_from_lengths([64 * 64])
+    a = orc.template_route_words("row_random", 500, 1, cu, 64 * 64, 4, 1)
+    assert np.array_equal(a, orc.template_route_words("row_random", 500, 1, cu, 64 * 64, 4, 1))
+    assert not np.array_equal(a, orc.template_route_words("row_random", 500, 2, cu, 64 * 64, 4, 1))
+    # over the 4 x 64 rows of 64 groups (last row: all 64 legal), FP16 frequency per position
+    counts = np.zeros(64)
+    for hk in range(4):
+        for m in range(48, 64):
+            word = int(a[hk, 0, m])
+            for j in range(m + 1):
+                counts[j] += 0 if (word >> j) & 1 else 1
+    frac = counts[:49] / 64.0
+    assert frac.min() > 0.25 and frac.max() < 0.75
+
+
 # ---------------------------------------------------------------- pin I
 @pytest.mark.parametrize("g", [1, 2, 3, 16])
 def test_pin_I_packer_decoder(g):
