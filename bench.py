@@ -3,7 +3,8 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: blockwise INT8 quantisation of Q and K (and V for the
 INT8 KV cache), route-word packing, the varlen/GQA work list and the fused
-attention kernel.  With --otf the quantiser calls drop out and the attention
+attention kernel (packing and the work list run on a second stream beside the
+quantiser).  With --otf the quantiser calls drop out and the attention
 kernel makes the INT8 operands on chip.  Default workload: the LLaMA-3.2-3B-shaped attention layer
 (batch 8, L = 4096, 24 query / 8 KV heads, d = 128, causal, FP16, 4 outlier
 channels, 64x64 tiles, g = 1, 75 % of the legal tile groups INT8).
@@ -173,6 +174,108 @@ def deviation_sweep(args, w, plan, q, k, v, cu, q_q, q_s, k_q, k_s, v_q, v_s, wo
         print(json.dumps(res), flush=True)
 
 
+def chunked_work(w, words):
+    """Legal (query, key) pairs of a chunked-prefill / decode call per route: the
+    queries are the last Lq of Lk positions (key j legal for query i iff
+    j <= Lk - Lq + i), counted exactly per score tile from the route words."""
+    G = w.num_q_heads // w.num_kv_heads
+    pairs16 = pairs8 = 0
+    for b, (Lq, Lk) in enumerate(zip(w.lengths, w.lengths_k)):
+        Lq, Lk, off = int(Lq), int(Lk), int(Lk) - int(Lq)
+        for m in range((Lq + 63) // 64):
+            i = np.arange(64 * m, min(64 * m + 64, Lq))
+            last = off + i                                   # last legal key of each row
+            for n in range((int(last.max())) // 64 + 1):
+                cnt = int(np.clip(np.minimum(last, min(64 * n + 63, Lk - 1)) - 64 * n + 1, 0, None).sum())
+                for hk in range(w.num_kv_heads):
+                    if (int(words[hk, b, m]) >> (n // w.g)) & 1:
+                        pairs8 += G * cnt
+                    else:
+                        pairs16 += G * cnt
+    d = w.head_dim
+    f_qk16, f_qk8, f_pv = 2 * d * pairs16, 2 * d * pairs8, 2 * d * (pairs16 + pairs8)
+    return dict(pairs=pairs16 + pairs8, pairs_int8=pairs8, ops=f_qk16 + f_qk8 + f_pv,
+                t_star=f_qk16 / P_FP16 + f_qk8 / P_INT8 + f_pv / P_FP16)
+
+
+def chunked_bench(args):
+    """Chunked prefill or decode over a resident INT8 KV cache (the cache is
+    quantised once, when written; a step quantises the new queries, packs their
+    route words, plans and runs the attention)."""
+    import torch
+    from mixed_precision_amd import tilemix as tm
+    from workloads import make_chunked_workload
+    dev = torch.device("cuda:0")
+    p = 0.75 if args.p is None else args.p
+    if args.chunked == "prefill":
+        w = make_chunked_workload(6, lengths_q=[512] * 8, lengths_k=[4096] * 8, num_q_heads=24, num_kv_heads=8,
+                                  head_dim=128, g=1, p=p, outliers=True, kv_int8=True,
+                                  name="chunk512_over_kv4096_B8_h24kv8_d128_int8kv")
+    else:
+        w = make_chunked_workload(7, lengths_q=[1] * 64, lengths_k=[4096] * 64, num_q_heads=24, num_kv_heads=8,
+                                  head_dim=128, g=1, p=p, outliers=True, kv_int8=True,
+                                  name="decode_B64_kv4096_h24kv8_d128_int8kv")
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    cu_k = torch.from_numpy(w.cu_seqlens_k).to(dev)
+    tr = torch.from_numpy(w.tile_route).to(dev)
+    N, Hq, d = w.q.shape
+    Hk, B = w.num_kv_heads, w.batch
+    k8, k_s = tm.tilemix_quantize_blockwise(k, cu_k, w.max_seqlen_k, 64)      # the resident INT8 cache
+    v8, v_s = tm.tilemix_quantize_blockwise(v, cu_k, w.max_seqlen_k, 64)
+    nbq = (w.max_seqlen + w.blk_q - 1) // w.blk_q
+    q_q = torch.empty((N, Hq, d), dtype=torch.int8, device=dev)
+    q_s = torch.empty((Hq, B, nbq), dtype=torch.float32, device=dev)
+    words = torch.empty((Hk, B, w.T), dtype=torch.int64, device=dev)
+    out = torch.empty((N, Hq, d), dtype=torch.float16, device=dev)
+    plan = tm.AttnPlan(tm.AttnProblem(B, w.max_seqlen, Hq, Hk, d, w.g, w.blk_q, w.sm_scale, True, False, False,
+                                      w.max_seqlen_k), dev)
+    stream = torch.cuda.current_stream()
+    kw = dict(cu_seqlens_k=cu_k, max_seqlen_k=w.max_seqlen_k)
+    tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream, **kw)
+    work = chunked_work(w, words.cpu().numpy().view(np.uint64))
+
+    def step(ev=None):
+        tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
+        tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream, **kw)
+        plan.schedule(cu, stream=stream, cu_seqlens_k=cu_k)
+        if ev is not None:
+            ev[0].record(stream)
+        plan.run_planned(q, k8, v8, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream,
+                         cu_seqlens_k=cu_k)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    t_attn = float(np.mean(attn_ms)) * 1e-3
+    # bytes every operand once: the INT8 cache (K8, V8 and their scales), fp16 Q, its int8 copy and scales,
+    # route words, fp16 output
+    kv_bytes = 2 * int(w.cu_seqlens_k[-1]) * Hk * d + 2 * 4 * Hk * B * w.T_k
+    q_bytes = N * Hq * d * (2 + 1) + 4 * Hq * B * nbq + 8 * Hk * B * w.T
+    bytes_ = kv_bytes + q_bytes + 2 * N * Hq * d
+    res = {"metric": f"chunked {args.chunked} over an INT8 KV cache: new tokens/s", "value": N / (ms_per_step * 1e-3),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+           "higher_is_better": True, "data": "synthetic",
+           "config": {"workload": w.name, "batch": B, "query_tokens": N, "keys_per_sequence": int(w.lengths_k[0]),
+                      "num_q_heads": Hq, "num_kv_heads": Hk, "head_dim": d, "int8_pair_fraction":
+                      work["pairs_int8"] / work["pairs"]},
+           "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
+           "roofline_mfma": {"achieved": work["ops"] / t_attn / 1e12, "peak": work["ops"] / work["t_star"] / 1e12,
+                             "unit": "TFLOP/s", "frac": work["t_star"] / t_attn},
+           "roofline_hbm": {"achieved": bytes_ / t_attn / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                            "frac": bytes_ / t_attn / HBM_PEAK, "algorithmic_bytes": bytes_}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +292,9 @@ def main():
     ap.add_argument("--template", type=str, default=None,
                     help="with --deviation-sweep: route by a static template (band, global, row_random, "
                          "aligned_sparse, bigbird, sptrans) instead of Bernoulli tile groups")
+    ap.add_argument("--chunked", choices=["prefill", "decode"], default=None,
+                    help="instead of the bench line: chunked prefill (512 new tokens over 4096 cached, batch 8) "
+                         "or decode (1 new token over 4096 cached, batch 64) on an INT8 KV cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -208,6 +314,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.chunked:
+        chunked_bench(args)
         return
     from mixed_precision_amd import tilemix as tm
     from workloads import config
@@ -242,14 +351,22 @@ def main():
     tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
     work = work_model(w, words.cpu().numpy().view(np.uint64))
 
+    # The route words and the work list depend only on the routing template and
+    # cu_seqlens: they are built on a second stream (default priority) while the
+    # quantiser streams Q and K, and the attention waits for both.
+    side = torch.cuda.Stream(device=dev)
+
     def step(ev=None):
+        side.wait_stream(stream)                 # the previous step's attention has read words / work list
+        with torch.cuda.stream(side):
+            tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=side)
+            plan.schedule(cu, stream=side)
         if not args.otf:
             tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
             tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
         if w.kv_int8:
             tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
-        tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
-        plan.schedule(cu, stream=stream)
+        stream.wait_stream(side)
         if ev is not None:
             ev[0].record(stream)
         if w.kv_int8:
