@@ -235,14 +235,18 @@ def chunked_bench(args):
     tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream, **kw)
     work = chunked_work(w, words.cpu().numpy().view(np.uint64))
 
-    def step(ev=None):
+    def step(ev=None, stream=stream):
         tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
         tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream, **kw)
-        plan.schedule(cu, stream=stream, cu_seqlens_k=cu_k)
+        if args.chunked == "prefill":
+            plan.schedule(cu, stream=stream, cu_seqlens_k=cu_k)
         if ev is not None:
             ev[0].record(stream)
-        plan.run_planned(q, k8, v8, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream,
-                         cu_seqlens_k=cu_k)
+        if args.chunked == "prefill":
+            plan.run_planned(q, k8, v8, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream,
+                             cu_seqlens_k=cu_k)
+        else:   # one call: decode needs no work list, and the library skips building it
+            plan.run(q, k8, v8, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream, cu_seqlens_k=cu_k)
         if ev is not None:
             ev[1].record(stream)
 
@@ -256,6 +260,20 @@ def chunked_bench(args):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in evs]
+    eager_ms = ms_per_step
+    if args.graph:
+        # the step's launches captured once in a HIP graph and replayed: no per-launch host work
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(stream=torch.cuda.current_stream())
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     t_attn = float(np.mean(attn_ms)) * 1e-3
     # bytes every operand once: the INT8 cache (K8, V8 and their scales), fp16 Q, its int8 copy and scales,
     # route words, fp16 output
@@ -264,7 +282,7 @@ def chunked_bench(args):
     bytes_ = kv_bytes + q_bytes + 2 * N * Hq * d
     res = {"metric": f"chunked {args.chunked} over an INT8 KV cache: new tokens/s", "value": N / (ms_per_step * 1e-3),
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-           "higher_is_better": True, "data": "synthetic",
+           "higher_is_better": True, "data": "synthetic", "hip_graph": bool(args.graph), "ms_per_step_eager": eager_ms,
            "config": {"workload": w.name, "batch": B, "query_tokens": N, "keys_per_sequence": int(w.lengths_k[0]),
                       "num_q_heads": Hq, "num_kv_heads": Hk, "head_dim": d, "int8_pair_fraction":
                       work["pairs_int8"] / work["pairs"]},
@@ -295,6 +313,7 @@ def main():
     ap.add_argument("--chunked", choices=["prefill", "decode"], default=None,
                     help="instead of the bench line: chunked prefill (512 new tokens over 4096 cached, batch 8) "
                          "or decode (1 new token over 4096 cached, batch 64) on an INT8 KV cache")
+    ap.add_argument("--graph", action="store_true", help="with --chunked: replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

@@ -151,6 +151,11 @@ int32_t validate_tensors(const tilemix_attn_params* p, const tilemix_attn_tensor
 
 enum class Mode { kPlanAndRun, kPlanOnly, kRunOnly };
 
+// Calls the decode kernel takes (see launch_attn): it needs no work list.
+bool decode_call(const tilemix_attn_params* p, const int32_t* cu_k, bool debug) {
+  return cu_k && p->max_seqlen == 1 && p->num_q_heads / p->num_kv_heads <= 16 && !p->otf_quant && !debug;
+}
+
 int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t, const int32_t* cu_seqlens,
                     const int32_t* cu_seqlens_k, void* workspace, size_t workspace_bytes, const tilemix_debug* dbg,
                     hipStream_t stream, Mode mode) {
@@ -207,7 +212,7 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
   sa.segidx = reinterpret_cast<int32_t*>(ws + d.ws.segidx_off);
   sa.order = reinterpret_cast<int32_t*>(ws + d.ws.order_off);
   hipError_t e = hipSuccess;
-  if (mode != Mode::kRunOnly) {
+  if (mode == Mode::kPlanOnly || (mode == Mode::kPlanAndRun && !decode_call(p, cu_seqlens_k, dbg != nullptr))) {
     e = launch_schedule(sa, stream);
     if (e != hipSuccess) return hip_status(e, "work-list launch");
     if (mode == Mode::kPlanOnly) return ok();
@@ -312,7 +317,18 @@ hipError_t launch_attn_d128_kv1(const AttnArgs&, int64_t, bool, hipStream_t);
 hipError_t launch_attn_d64_otf(const AttnArgs&, int64_t, bool, hipStream_t);
 hipError_t launch_attn_d128_otf(const AttnArgs&, int64_t, bool, hipStream_t);
 
+hipError_t launch_attn_decode(const AttnArgs&, hipStream_t);
+
+// Decode (chunked with one query per sequence: max_seqlen = 1) with the query
+// heads of a KV head fitting one 16-row MFMA block goes to the decode kernel
+// (heads as rows, waves splitting the keys); everything else, and the debug
+// products, to the fused prefill kernel.
+bool decode_shape(const AttnArgs& a, bool debug) {
+  return a.cu_k && a.max_seqlen == 1 && a.G <= 16 && !a.otf && !debug;
+}
+
 hipError_t launch_attn(const AttnArgs& a, int64_t nslots, bool debug, hipStream_t s) {
+  if (decode_shape(a, debug)) return launch_attn_decode(a, s);
   if (a.D == 64) {
     if (a.kv_int8) return launch_attn_d64_kv1(a, nslots, debug, s);
     return a.otf ? launch_attn_d64_otf(a, nslots, debug, s) : launch_attn_d64_kv0(a, nslots, debug, s);
