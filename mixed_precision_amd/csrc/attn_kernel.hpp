@@ -103,6 +103,14 @@ struct Attn {
   // (2^15 < 65504).  INT8 V: p * v_scale goes to fp16, so 2^8 keeps it finite
   // for any |V| below 32,500 (v_scale < 256).
   static constexpr float kSlack = KVI8 ? 8.0f : 15.0f;
+  // When the reference moves, FP16 V sets it kOver above the new maximum, so
+  // the row's maximum can grow by kOver + kSlack before the next rescale
+  // (fewer O rescales on rows whose maximum keeps rising).  The largest p is
+  // then >= 2^-kOver: the terms within 14 - kOver of the maximum keep fp16's
+  // full precision, and the smaller ones fall into its subnormal range, whose
+  // absolute step is 2^-24.  With near one-hot rows (outlier channels) an
+  // overshoot of 8 doubled the worst output error; 4 left it unchanged.
+  static constexpr float kOver = KVI8 ? 0.0f : 4.0f;
   static constexpr int NDS = D / 32;       // fp16 MFMA k-steps over d
   static constexpr int NDS8 = D / 64;      // int8 MFMA k-steps over d
   static constexpr int NDB = D / 16;       // 16-row blocks of d in O^T
@@ -308,10 +316,14 @@ struct Attn {
       // a single element of an ext_vector (it reads element 0).
       const f32x4 a = __builtin_bit_cast(f32x4, S[j][0]);
       const f32x4 b = __builtin_bit_cast(f32x4, S[j][1]);
-      lm[j] = __builtin_elementwise_maximum(
-          __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[0], a[1]), __builtin_elementwise_maximum(a[2], a[3])),
-          __builtin_elementwise_maximum(__builtin_elementwise_maximum(b[0], b[1]), __builtin_elementwise_maximum(b[2], b[3])));
-      up |= lm[j] * cj[j] > mref[j] + kSlack;
+      // three-input max tree (v_maximum3): 4 instructions for 8 values
+      const float t0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[0], a[1]), a[2]);
+      const float t1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[3], b[0]), b[1]);
+      const float t2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(b[2], b[3]), t0);
+      lm[j] = __builtin_elementwise_maximum(t1, t2);
+      // lm c - m_ref > kSlack in one fma (mref = -inf gives +inf: a first
+      // finite score always moves the reference)
+      up |= __builtin_fmaf(lm[j], cj[j], -mref[j]) > kSlack;
     }
     if (__any(up)) {
 #pragma unroll
@@ -320,8 +332,9 @@ struct Attn {
         mx = rows4_max(mx);
         const float tmax = mx * cj[j];
         const bool moved = tmax > mref[j] + kSlack;
-        const float alpha = moved ? __builtin_amdgcn_exp2f(mref[j] - tmax) : 1.0f;
-        mref[j] = moved ? tmax : mref[j];
+        const float tnew = tmax + kOver;
+        const float alpha = moved ? __builtin_amdgcn_exp2f(mref[j] - tnew) : 1.0f;
+        mref[j] = moved ? tnew : mref[j];
         lrow[j] *= alpha;
         if (__any(moved)) {
 #pragma unroll
