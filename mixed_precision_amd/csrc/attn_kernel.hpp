@@ -306,8 +306,12 @@ struct Attn {
   // take the reduction over the query's 4 lanes, move the reference and
   // rescale l and the accumulator (the same decision as reducing first, since
   // the reduced max exceeds the bound exactly when some lane's max does).
+  // Row sums: with an INT8 V cache each lane adds its p (before the v-scale)
+  // into lrow; with fp16 V the P.V step accumulates them on the MFMA into lacc
+  // (an all-ones A operand times P^T: every row of lacc holds the query's sum
+  // over the half's 32 keys), which takes the adds off the VALU.
   static TM_DEV void softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float vsc, float (&mref)[QB],
-                             float (&lrow)[QB], f32x4 (&O)[QB][NDB], f16x8 (&P)[QB]) {
+                             float (&lrow)[QB], f32x4 (&lacc)[QB], f32x4 (&O)[QB][NDB], f16x8 (&P)[QB]) {
     float lm[QB];
     bool up = false;
 #pragma unroll
@@ -335,8 +339,9 @@ struct Attn {
         const float tnew = tmax + kOver;
         const float alpha = moved ? __builtin_amdgcn_exp2f(mref[j] - tnew) : 1.0f;
         mref[j] = moved ? tnew : mref[j];
-        lrow[j] *= alpha;
+        if (KVI8) lrow[j] *= alpha;
         if (__any(moved)) {
+          if (!KVI8) lacc[j] *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) O[j][db] *= alpha;
         }
@@ -359,19 +364,19 @@ struct Attn {
           lsum += p0 + p1;
         } else {
           hv = f16x2{(f16)p0, (f16)p1};
-          lsum = __builtin_amdgcn_fdot2(hv, f16x2{(f16)1.0f, (f16)1.0f}, lsum, false);
         }
         pk[t] = __builtin_bit_cast(uint32_t, hv);
       }
       P[j] = __builtin_bit_cast(f16x8, pk);
-      lrow[j] += lsum;
+      if (KVI8) lrow[j] += lsum;
     }
   }
 
   // --- O^T += V^T P^T for half h.  Lane (c, gq) needs, for channel db*16+c,
   // keys 32h+4gq+0..3 (lo) and 32h+16+4gq+0..3 (hi); each comes from one
   // ds_read_b64_tr_b16 whose 16 lanes address 4 keys x 16 channels.
-  static TM_DEV void pv(const char* vl, int h, const f16x8 (&P)[QB], f32x4 (&O)[QB][NDB], int lane) {
+  static TM_DEV void pv(const char* vl, int h, const f16x8 (&P)[QB], f32x4 (&O)[QB][NDB], f32x4 (&lacc)[QB],
+                        int lane) {
     const int gq = lane >> 4, jl = lane & 15;
     // key 32h + 16e + (4gq + jl/4), channels db*16 + 4*(jl%4) .. +3
     const char* base = vl + LV::lane(4 * gq + (jl >> 2)) + 8 * (jl & 3);
@@ -382,6 +387,11 @@ struct Attn {
       const f16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
       for (int j = 0; j < QB; ++j) O[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, P[j], O[j][db], 0, 0, 0);
+    }
+    if (!KVI8) {
+      const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+#pragma unroll
+      for (int j = 0; j < QB; ++j) lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[j], lacc[j], 0, 0, 0);
     }
   }
 };
@@ -526,10 +536,12 @@ void attn_prefill_kernel(const AttnArgs a) {
   // ---- online-softmax state (log2 domain), output accumulator O^T
   f32x4 O[QB][NDB];
   float mref[QB], lrow[QB];
+  f32x4 lacc[QB];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     mref[j] = -INFINITY;
     lrow[j] = 0.0f;
+    lacc[j] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[j][db] = f32x4{0, 0, 0, 0};
   }
@@ -658,9 +670,9 @@ void attn_prefill_kernel(const AttnArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
       f16x8 P[QB];
-      A::softmax(S, cj, vsc, mref, lrow, O, P);
+      A::softmax(S, cj, vsc, mref, lrow, lacc, O, P);
       __builtin_amdgcn_s_setprio(1);
-      A::pv(vl, h, P, O, lane);
+      A::pv(vl, h, P, O, lacc, lane);
       __builtin_amdgcn_s_setprio(0);
     }
     if (KVI8) {
@@ -694,8 +706,8 @@ void attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     if (j >= nh) continue;
-    float l = lrow[j];
-    l = rows4_sum(l);
+    // the row's sum: the lanes' partial sums (INT8 V), or any row of lacc
+    const float l = KVI8 ? rows4_sum(lrow[j]) : lacc[j][0];
     const float inv = 1.0f / l;
     if (!qb_valid(j)) continue;
     // (row in tile) * Hq + (head in chunk)
