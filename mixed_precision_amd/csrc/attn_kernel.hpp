@@ -310,7 +310,9 @@ struct Attn {
   // into lrow; with fp16 V the P.V step accumulates them on the MFMA into lacc
   // (an all-ones A operand times P^T: every row of lacc holds the query's sum
   // over the half's 32 keys), which takes the adds off the VALU.
-  static TM_DEV void softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float vsc, float (&mref)[QB],
+  // The reference max is kept negated (nref = -m_ref) so that every exponent
+  // is one fma with it as the addend.
+  static TM_DEV void softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float vsc, float (&nref)[QB],
                              float (&lrow)[QB], f32x4 (&lacc)[QB], f32x4 (&O)[QB][NDB], f16x8 (&P)[QB]) {
     float lm[QB];
     bool up = false;
@@ -325,9 +327,9 @@ struct Attn {
       const float t1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[3], b[0]), b[1]);
       const float t2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(b[2], b[3]), t0);
       lm[j] = __builtin_elementwise_maximum(t1, t2);
-      // lm c - m_ref > kSlack in one fma (mref = -inf gives +inf: a first
+      // lm c - m_ref > kSlack in one fma (m_ref = -inf gives +inf: a first
       // finite score always moves the reference)
-      up |= __builtin_fmaf(lm[j], cj[j], -mref[j]) > kSlack;
+      up |= __builtin_fmaf(lm[j], cj[j], nref[j]) > kSlack;
     }
     if (__any(up)) {
 #pragma unroll
@@ -335,10 +337,10 @@ struct Attn {
         float mx = lm[j];
         mx = rows4_max(mx);
         const float tmax = mx * cj[j];
-        const bool moved = tmax > mref[j] + kSlack;
+        const bool moved = tmax + nref[j] > kSlack;
         const float tnew = tmax + kOver;
-        const float alpha = moved ? __builtin_amdgcn_exp2f(mref[j] - tnew) : 1.0f;
-        mref[j] = moved ? tnew : mref[j];
+        const float alpha = moved ? __builtin_amdgcn_exp2f(-(nref[j] + tnew)) : 1.0f;
+        nref[j] = moved ? -tnew : nref[j];
         if (KVI8) lrow[j] *= alpha;
         if (__any(moved)) {
           if (!KVI8) lacc[j] *= alpha;
@@ -356,8 +358,8 @@ struct Attn {
       u32x4 pk;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t], cj[j], -mref[j]));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t + 1], cj[j], -mref[j]));
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t], cj[j], nref[j]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t + 1], cj[j], nref[j]));
         f16x2 hv;
         if (KVI8) {
           hv = f16x2{(f16)(p0 * vsc), (f16)(p1 * vsc)};
@@ -441,7 +443,11 @@ void attn_prefill_kernel(const AttnArgs a) {
   auto qb_row = [&](int j) { return qb_rb(j) * 16 + c; };                           // query offset in tile
   auto qb_valid = [&](int j) { return (j < nh) && (m * kTile + qb_row(j) < L); };
   // q-block scale times sm_scale * log2(e): the INT8 score factor is sqs * k_scale
-  // (wave-uniform values, kept in scalar registers)
+  // (wave-uniform values, kept in scalar registers).  Both factors are kept at
+  // or above sqrt(FLT_MIN) (kScaleFloor), so their product stays a positive
+  // normal number and a (caller-supplied) zero scale cannot turn a masked -inf
+  // into NaN; scales made by the quantiser are far above that floor.
+  constexpr float kScaleFloor = 1.0842022e-19f;
   float sqs[QB];
   if (!OTF) {
 #pragma unroll
@@ -450,7 +456,7 @@ void attn_prefill_kernel(const AttnArgs a) {
       float sq = 1.0f;
       if (j < nh && blk_start < L)
         sq = a.q_scale[((int64_t)qb_head(j) * a.batch + b) * a.nbq + blk_start / a.blk_q];
-      sqs[j] = sgpr_f32(sq * a.sm_log2);
+      sqs[j] = sgpr_f32(__builtin_elementwise_maximum(sq * a.sm_log2, kScaleFloor));
     }
   }
 
@@ -535,11 +541,11 @@ void attn_prefill_kernel(const AttnArgs a) {
 
   // ---- online-softmax state (log2 domain), output accumulator O^T
   f32x4 O[QB][NDB];
-  float mref[QB], lrow[QB];
+  float nref[QB], lrow[QB];   // -(reference max), row sums (INT8 V)
   f32x4 lacc[QB];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    mref[j] = -INFINITY;
+    nref[j] = INFINITY;
     lrow[j] = 0.0f;
     lacc[j] = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -569,7 +575,7 @@ void attn_prefill_kernel(const AttnArgs a) {
         const int hj = (wave * nh + j) >> 2;
         sq = uniform(block_scale(max(max(qam[hj * 4], qam[hj * 4 + 1]), max(qam[hj * 4 + 2], qam[hj * 4 + 3]))));
       }
-      sqs[j] = sgpr_f32(sq * a.sm_log2);
+      sqs[j] = sgpr_f32(__builtin_elementwise_maximum(sq * a.sm_log2, kScaleFloor));
       const float rs = __fdiv_rn(1.0f, sq);
       const int64_t tok = (int64_t)seq0 + m * kTile + qb_row(j);
       const bool valid = qb_valid(j);
@@ -620,8 +626,9 @@ void attn_prefill_kernel(const AttnArgs a) {
     // masked -inf into NaN
     float cj[QB];
     if (rc) {
+      const float kc = __builtin_elementwise_maximum(ksc, kScaleFloor);
 #pragma unroll
-      for (int j = 0; j < QB; ++j) cj[j] = __builtin_elementwise_maximum(sqs[j] * ksc, 1.17549435e-38f);
+      for (int j = 0; j < QB; ++j) cj[j] = sqs[j] * kc;
     } else {
       const float c16 = __builtin_elementwise_maximum(KVI8 ? ksc * a.sm_log2 : a.sm_log2, 1.17549435e-38f);
 #pragma unroll
@@ -670,7 +677,7 @@ void attn_prefill_kernel(const AttnArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
       f16x8 P[QB];
-      A::softmax(S, cj, vsc, mref, lrow, lacc, O, P);
+      A::softmax(S, cj, vsc, nref, lrow, lacc, O, P);
       __builtin_amdgcn_s_setprio(1);
       A::pv(vl, h, P, O, lacc, lane);
       __builtin_amdgcn_s_setprio(0);
@@ -683,10 +690,11 @@ void attn_prefill_kernel(const AttnArgs a) {
     // on-the-fly mode: this wave's max |k| of an INT8 next tile
     if (OTF && rnext && !last) A::k_partial_amax(next, wave, lane);
     __syncthreads();
-    if (--left == 0) {
-      left = g;
-      wsh >>= 1;
-    }
+    // next tile's group, in integer arithmetic (left >= 1; a compare here
+    // became a VALU select and a readfirstlane)
+    const int adv = 1 - min(left - 1, 1);
+    wsh >>= adv;
+    left += adv * g - 1;
   };
 #pragma unroll 1
   for (int n = 0;; n += 2) {
@@ -714,7 +722,7 @@ void attn_prefill_kernel(const AttnArgs a) {
     const uint32_t e = (uint32_t)(qb_row(j) * a.Hq + ((wave * nh + j) >> 2));
     // log-sum-exp of the row's scores: the state is in log2 units of the
     // scaled scores, so LSE = (m_ref + log2 l) ln 2
-    if (lse_base && gq == 0) lse_base[e] = (mref[j] + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+    if (lse_base && gq == 0) lse_base[e] = (__builtin_amdgcn_logf(l) - nref[j]) * 0.6931471805599453f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x4 r = O[j][db] * inv;
