@@ -313,7 +313,8 @@ def main():
     ap.add_argument("--chunked", choices=["prefill", "decode"], default=None,
                     help="instead of the bench line: chunked prefill (512 new tokens over 4096 cached, batch 8) "
                          "or decode (1 new token over 4096 cached, batch 64) on an INT8 KV cache")
-    ap.add_argument("--graph", action="store_true", help="with --chunked: replay the step as a captured HIP graph")
+    ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph (attention times "
+                    "still come from the eager steps' events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -371,21 +372,27 @@ def main():
     work = work_model(w, words.cpu().numpy().view(np.uint64))
 
     # The route words and the work list depend only on the routing template and
-    # cu_seqlens: they are built on a second stream (default priority) while the
-    # quantiser streams Q and K, and the attention waits for both.
+    # cu_seqlens: they are built on a second stream while the quantiser streams Q
+    # on the main stream and K (and V) on a third; the attention waits for all.
+    # Every stream has the default priority.
     side = torch.cuda.Stream(device=dev)
+    kvs = torch.cuda.Stream(device=dev)
 
-    def step(ev=None):
+    def step(ev=None, stream=stream):
         side.wait_stream(stream)                 # the previous step's attention has read words / work list
+        kvs.wait_stream(stream)                  # ... and K8 / V8
         with torch.cuda.stream(side):
             tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=side)
             plan.schedule(cu, stream=side)
+        with torch.cuda.stream(kvs):
+            if not args.otf:
+                tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=kvs)
+            if w.kv_int8:
+                tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=kvs)
         if not args.otf:
             tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
-            tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
-        if w.kv_int8:
-            tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
         stream.wait_stream(side)
+        stream.wait_stream(kvs)
         if ev is not None:
             ev[0].record(stream)
         if w.kv_int8:
@@ -408,6 +415,21 @@ def main():
     wall = time.perf_counter() - t0
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     ms_per_step = wall * 1e3 / args.steps
+    eager_ms = ms_per_step
+    if args.graph:
+        # the same step captured once in a HIP graph (three streams forked from
+        # and joined to the capture stream) and replayed
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(stream=torch.cuda.current_stream())
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     t_attn = float(np.mean(attn_ms)) * 1e-3
     achieved = work["ops"] / t_attn
     blended_peak = work["ops"] / work["t_star"]
@@ -429,6 +451,7 @@ def main():
                      "note": "peak = blended MFMA peak of this launch's mix: ops / (F_qk16/P16 + F_qk8/P8 + F_pv/P16)"},
         "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
         "attn_tokens_per_s": N / t_attn, "t_star_ms": work["t_star"] * 1e3,
+        "hip_graph": bool(args.graph), "ms_per_step_eager": eager_ms,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

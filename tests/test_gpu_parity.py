@@ -628,6 +628,57 @@ def test_decode_step_graph_replay(gp):
     assert ma <= MAX_ABS and rf <= REL_FRO
 
 
+def test_prefill_step_three_streams_graph_replay(gp):
+    """A prefill step as the benchmark runs it: route packing and the work list
+    on one stream, K quantised on a second, Q on the capture stream, then the
+    planned attention after joining all three.  Captured in a HIP graph: every
+    replay, with eager steps and synchronisations between replays, gives the
+    eager step's bits, and the eager step matches the oracle."""
+    import torch
+    _announce("prefill step three streams graph replay")
+    w = make_workload(537, lengths=[64 * 5 + 17, 64 * 3, 29], num_q_heads=6, num_kv_heads=2, head_dim=128, g=1,
+                      p=0.75, outliers=True)
+    t = gp.prepare(w)
+    tm = gp.tm
+    plan = tm.AttnPlan(tm.AttnProblem(w.batch, w.max_seqlen, 6, 2, 128, 1, w.blk_q, w.sm_scale, False, True, False),
+                       "cuda:0")
+    out = torch.empty((int(w.cu_seqlens[-1]), 6, 128), dtype=torch.float32, device="cuda:0")
+    side, kvs = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def step(stream):
+        side.wait_stream(stream)
+        kvs.wait_stream(stream)
+        with torch.cuda.stream(side):
+            tm.tilemix_build_route_mask(t["tile_route"], t["cu"], w.max_seqlen, w.g, t["words"], stream=side)
+            plan.schedule(t["cu"], stream=side)
+        with torch.cuda.stream(kvs):
+            tm.tilemix_quantize_blockwise(t["k"], t["cu"], w.max_seqlen, 64, t["k_q"], t["k_s"], stream=kvs)
+        tm.tilemix_quantize_blockwise(t["q"], t["cu"], w.max_seqlen, w.blk_q, t["q_q"], t["q_s"], stream=stream)
+        stream.wait_stream(side)
+        stream.wait_stream(kvs)
+        plan.run_planned(t["q"], t["k"], t["v"], t["q_q"], t["q_s"], t["k_q"], t["k_s"], t["cu"], t["words"], out,
+                         stream=stream)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for _ in range(3):
+        out.zero_()
+        t["words"].zero_()
+        step(torch.cuda.current_stream())          # eager work between replays
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        t["words"].fill_(-1)                       # the replay must rebuild them
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    ma, rf = gp.errors(eager.cpu().numpy(), orc.attn_prefill(oracle_inputs(w)))
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
 def test_attn_chunked_debug_bitexact(gp):
     """Chunked prefill: INT32 score tiles, visits and decoded routes bit-exact
     (the causal edge cuts two key tiles for some query tiles)."""
