@@ -218,6 +218,31 @@ struct Attn {
       r.v[i] = bload16(rv, off);
     }
   }
+  // INT8 KV cache, LDS staging: the raw int8 K and V tiles land in LDS by
+  // lds-loads in their natural [row][D] layout (RAW_BYTES: K, then V).  The
+  // loads cover the same 16-byte chunks stage_load does: instruction i of wave
+  // w fills bytes 1024 w + 4096 i .. +1023 of each, lane l chunk id =
+  // tid + 256 i at 16 id.  The widening pass then reads them back
+  // (stage_from_lds) and stage_store writes the stage, so no staging registers
+  // stay live while a tile is computed.
+  static constexpr int RAW_BYTES = 2 * 64 * D;
+  static TM_DEV void raw_dma(char* raw, int tid, int wave, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                             uint32_t stride) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const int id = tid + 256 * i;
+      const uint32_t off = (id / (D / 16)) * stride + (id % (D / 16)) * 16;
+      bload16_lds(rk, off, raw + 1024 * wave + 4096 * i);
+      bload16_lds(rv, off, raw + 64 * D + 1024 * wave + 4096 * i);
+    }
+  }
+  static TM_DEV void stage_from_lds(Stage& r, int tid, const char* raw) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      r.k[i] = *reinterpret_cast<const u32x4*>(raw + 16 * (tid + 256 * i));
+      r.v[i] = *reinterpret_cast<const u32x4*>(raw + 64 * D + 16 * (tid + 256 * i));
+    }
+  }
   static TM_DEV void stage_store(const Stage& r, int route, int tid, char* kl, char* vl) {
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
@@ -406,10 +431,18 @@ void attn_prefill_kernel(const AttnArgs a) {
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
   // two stages (K tile, then V tile) as two LDS objects: with a fixed object
   // per access the compiler can tell the loads into one stage from reads of
-  // the other and does not make those reads wait for the loads
+  // the other and does not make those reads wait for the loads.
+  //   INT8 KV cache, up to 2 heads per item: the next tile travels through
+  //   registers (staged while the current one is computed) into the other stage.
+  //   INT8 KV cache, 3 heads per item (RAWST): those 16 staging registers do not
+  //   fit beside three q-blocks, so lds-loads bring the raw int8 tile into `raw`
+  //   while the one stage is computed, and it is widened into the stage between
+  //   two barriers.
+  constexpr bool RAWST = KVI8 && QB == 3;
   constexpr int STAGE = A::KBYTES + A::VBYTES + (OTF ? 16 : 0);
   __shared__ __attribute__((aligned(1024))) char stA[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stB[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stB[RAWST ? 16 : STAGE];
+  __shared__ __attribute__((aligned(1024))) char raw[RAWST ? A::RAW_BYTES : 16];
   // on-the-fly mode: the current INT8 tile's K, and per-wave Q-block maxima
   __shared__ __attribute__((aligned(16))) char k8s[OTF ? A::L8::BYTES : 16];
   __shared__ uint32_t qam[OTF ? 3 * 4 : 1];
@@ -527,9 +560,13 @@ void attn_prefill_kernel(const AttnArgs a) {
   // group still covers (groups past bit 63 shift in zeros = FP16).
   uint64_t wsh = word;
   int left = g;
-  // start the loads of tile n (K in its route's form, and V) into stage `sg`
+  // start the loads of tile n (K in its route's form, and V) into stage `sg`;
+  // INT8 KV cache: into the staging registers, or the raw int8 tile into `raw`
   auto fetch = [&](int n, int route, typename A::Stage& st, char* sg, bool empty) __attribute__((always_inline)) {
-    if (KVI8) {
+    if (RAWST) {
+      A::raw_dma(raw, tid, wave, tile_rsrc(kbase, kv_stride, n, empty), tile_rsrc(vbase, kv_stride, n, empty),
+                 kv_stride);
+    } else if (KVI8) {
       A::stage_load(st, tid, tile_rsrc(kbase, kv_stride, n, empty), tile_rsrc(vbase, kv_stride, n, empty),
                     kv_stride);
     } else {
@@ -556,7 +593,7 @@ void attn_prefill_kernel(const AttnArgs a) {
   {
     typename A::Stage st;
     fetch(0, OTF ? 0 : (int)(wsh & 1), st, stA, false);
-    if (KVI8) {
+    if (KVI8 && !RAWST) {
       wait_vmem();
       A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES);
     }
@@ -564,6 +601,12 @@ void attn_prefill_kernel(const AttnArgs a) {
   wait_vmem();
   if (OTF && (wsh & 1)) A::k_partial_amax(stA, wave, lane);
   __syncthreads();
+  if (RAWST) {
+    typename A::Stage st;
+    A::stage_from_lds(st, tid, raw);
+    A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES);
+    lds_barrier();
+  }
 
   // on-the-fly mode: Q block scales and the INT8 Q operands (channels
   // 64 ds + 16 gq .. +15 of the lane's query row)
@@ -682,7 +725,7 @@ void attn_prefill_kernel(const AttnArgs a) {
       A::pv(vl, h, P, O, lacc, lane);
       __builtin_amdgcn_s_setprio(0);
     }
-    if (KVI8) {
+    if (KVI8 && !RAWST) {
       wait_vmem();
       A::stage_store(st, rnext, tid, next, next + A::KBYTES);
     }
@@ -690,17 +733,27 @@ void attn_prefill_kernel(const AttnArgs a) {
     // on-the-fly mode: this wave's max |k| of an INT8 next tile
     if (OTF && rnext && !last) A::k_partial_amax(next, wave, lane);
     __syncthreads();
+    // LDS staging: every wave is done with the stage and the raw next tile
+    // has landed; widen it into the stage (skipped after the last tile)
+    if (RAWST && !last) {
+      typename A::Stage st;
+      A::stage_from_lds(st, tid, raw);
+      A::stage_store(st, rnext, tid, next, next + A::KBYTES);
+      lds_barrier();
+    }
     // next tile's group, in integer arithmetic (left >= 1; a compare here
     // became a VALU select and a readfirstlane)
     const int adv = 1 - min(left - 1, 1);
     wsh >>= adv;
     left += adv * g - 1;
   };
+  // (LDS staging computes and refills its one stage)
+  char* const st2 = RAWST ? stA : stB;
 #pragma unroll 1
   for (int n = 0;; n += 2) {
-    tile(n, stA, stB);
+    tile(n, stA, st2);
     if (n + 1 > n_last) break;
-    tile(n + 1, stB, stA);
+    tile(n + 1, st2, stA);
     if (n + 2 > n_last) break;
   }
 

@@ -59,10 +59,15 @@ int32_t check_groups(int32_t max_seqlen_keys, int32_t g) {
   return TILEMIX_OK;
 }
 
-// Query heads per workgroup at most: 3 with fp16 K/V; 2 with the INT8 KV cache,
-// whose register staging of the next tile leaves too few VGPRs for 3 (spills in
-// the inner loop cost more than loading each K/V tile once more).
-int32_t max_heads_per_chunk(const tilemix_attn_params* p) { return p->kv_int8 ? 2 : 3; }
+// Query heads per work item.  fp16 K/V: up to 3.  INT8 KV cache: 3 when the
+// GQA ratio is a multiple of 3 (the 3-head kernel stages tiles through LDS,
+// which costs a serialized widening step per tile), else 2 (tiles staged in
+// registers; a 3 + 3 + 1 split of 7 heads measured slower than 2 + 2 + 2 + 1).
+int32_t max_heads_per_chunk(const tilemix_attn_params* p) {
+  if (!p->kv_int8) return 3;
+  const int32_t G = p->num_kv_heads > 0 ? p->num_q_heads / p->num_kv_heads : 1;
+  return G % 3 == 0 ? 3 : 2;
+}
 
 int32_t validate_attn_params(const tilemix_attn_params* p) {
   if (!p) return fail(TILEMIX_ERR_INVALID_ARG, "params is NULL");

@@ -213,6 +213,9 @@ SMALL = [
     ("mild_kv_int8", [500], 7, 1, 128, 2, "bernoulli", 0.5, True, 64, "mild"),
     # more sequences than the work-list planner keeps in LDS (global-scratch path)
     ("many_seqs_4100", [1 + (i * 37) % 70 for i in range(4100)], 2, 1, 64, 1, "bernoulli", 0.5, False, 64, False),
+    # INT8 KV cache with a GQA ratio of 3: three heads per item, tiles staged through LDS
+    ("kv_int8_gqa3_lds", [300, 64, 130, 1], 6, 2, 128, 2, "bernoulli", 0.5, True, 64, True),
+    ("kv_int8_gqa3_d64", [200, 77], 3, 1, 64, 1, "bernoulli", 0.6, True, 128, False),
 ]
 
 
@@ -245,7 +248,7 @@ def test_attn_small_full(gp, case):
             assert np.max(np.abs(got[s0, h] - v0)) <= 1e-3 * max(1.0, np.max(np.abs(v0)))
 
 
-@pytest.mark.parametrize("case", ["tiny", "gqa3_varlen", "kv_int8"])
+@pytest.mark.parametrize("case", ["tiny", "gqa3_varlen", "kv_int8", "kv_int8_gqa3"])
 def test_attn_debug_bitexact(gp, case):
     """INT32 score tiles bit-exact; every legal tile visited once, nothing else;
     the decoded route per visited tile equals the oracle's."""
@@ -258,10 +261,14 @@ def test_attn_debug_bitexact(gp, case):
         w = make_workload(450, lengths=[130, 300, 64], num_q_heads=6, num_kv_heads=2, head_dim=128, g=2,
                           p=0.6, outliers=True)
         seq, head = 1, 4
-    else:
+    elif case == "kv_int8":
         w = make_workload(451, lengths=[260, 90], num_q_heads=7, num_kv_heads=1, head_dim=128, g=1, p=0.5,
                           kv_int8=True)
         seq, head = 0, 5
+    else:   # three heads per item: the INT8 tiles are staged through LDS
+        w = make_workload(452, lengths=[200, 70], num_q_heads=3, num_kv_heads=1, head_dim=128, g=1, p=0.5,
+                          kv_int8=True, outliers=True)
+        seq, head = 0, 2
     t = gp.prepare(w)
     out, s32, visits, used = gp.attn_debug(w, t, seq=seq, q_head=head)
     torch.cuda.synchronize()
@@ -505,6 +512,8 @@ CHUNKED = [
     ("decode_gqa7_int8kv", [1] * 5, [1, 15, 129, 3000, 8191], 14, 2, 128, 4, 0.6, True, 64),
     ("decode_gqa16_fp16kv", [1] * 4, [7, 700, 2048, 5000], 16, 1, 128, 2, 0.4, False, 64),
     ("decode_gqa3_d64_int8kv", [1] * 3, [2, 333, 4097], 6, 2, 64, 2, 0.5, True, 64),
+    # chunked prefill, INT8 cache, GQA 3 (three heads per item, LDS staging)
+    ("chunk_int8kv_gqa3", [190, 64, 5], [900, 64, 700], 6, 2, 128, 1, 0.5, True, 64),
 ]
 
 
