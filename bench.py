@@ -223,6 +223,11 @@ def chunked_bench(args):
     Hk, B = w.num_kv_heads, w.batch
     k8, k_s = tm.tilemix_quantize_blockwise(k, cu_k, w.max_seqlen_k, 64)      # the resident INT8 cache
     v8, v_s = tm.tilemix_quantize_blockwise(v, cu_k, w.max_seqlen_k, 64)
+    if args.kv_layout == "head":
+        # head-major storage ([Hk][N][d], viewed as [N][Hk][d] through strides): a KV head's rows are contiguous,
+        # as in paged caches that keep each head's block of tokens together
+        k8 = k8.transpose(0, 1).contiguous().transpose(0, 1)
+        v8 = v8.transpose(0, 1).contiguous().transpose(0, 1)
     nbq = (w.max_seqlen + w.blk_q - 1) // w.blk_q
     q_q = torch.empty((N, Hq, d), dtype=torch.int8, device=dev)
     q_s = torch.empty((Hq, B, nbq), dtype=torch.float32, device=dev)
@@ -283,7 +288,7 @@ def chunked_bench(args):
     res = {"metric": f"chunked {args.chunked} over an INT8 KV cache: new tokens/s", "value": N / (ms_per_step * 1e-3),
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
            "higher_is_better": True, "data": "synthetic", "hip_graph": bool(args.graph), "ms_per_step_eager": eager_ms,
-           "config": {"workload": w.name, "batch": B, "query_tokens": N, "keys_per_sequence": int(w.lengths_k[0]),
+           "config": {"workload": w.name, "batch": B, "query_tokens": N, "kv_layout": args.kv_layout, "keys_per_sequence": int(w.lengths_k[0]),
                       "num_q_heads": Hq, "num_kv_heads": Hk, "head_dim": d, "int8_pair_fraction":
                       work["pairs_int8"] / work["pairs"]},
            "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
@@ -313,6 +318,8 @@ def main():
     ap.add_argument("--chunked", choices=["prefill", "decode"], default=None,
                     help="instead of the bench line: chunked prefill (512 new tokens over 4096 cached, batch 8) "
                          "or decode (1 new token over 4096 cached, batch 64) on an INT8 KV cache")
+    ap.add_argument("--kv-layout", choices=["token", "head"], default="token",
+                    help="with --chunked: INT8 cache stored token-major [N][Hk][d] or head-major [Hk][N][d]")
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph (attention times "
                     "still come from the eager steps' events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
