@@ -243,7 +243,33 @@ struct Attn {
       r.v[i] = *reinterpret_cast<const u32x4*>(raw + 64 * D + 16 * (tid + 256 * i));
     }
   }
-  static TM_DEV void stage_store(const Stage& r, int route, int tid, char* kl, char* vl) {
+  // INT8 V: the tile's scale s_v = mv 2^E with E = min(exponent, 5) >= -24 and
+  // mv in [1, 16) (scales below 2^-24 take E = -24, mv = 1).  V is widened
+  // exactly to v8 2^E, the mantissa mv goes into P (log2 mv added in the
+  // exponent) and the row sum adds P / mv: the P.V numerator and the row sum
+  // then use the same rounded weights, as with fp16 V.
+  struct VSplit {
+    float lmv, rmv;   // log2 mv, 1 / mv
+    f16x2 s2, b2;     // 2^E and -1152 2^E for the widening fma
+  };
+  static TM_DEV VSplit vsplit(float vsc) {
+    int E = -24;
+    float mv = 1.0f;
+    if (vsc >= 0x1p-24f && vsc <= 65504.0f) {
+      E = min((int)((__builtin_bit_cast(uint32_t, vsc) >> 23) & 0xFF) - 127, 5);
+      mv = __builtin_ldexpf(vsc, -E);
+    }
+    const float p2 = __builtin_ldexpf(1.0f, E);
+    VSplit v;
+    v.lmv = __builtin_amdgcn_logf(mv);
+    v.rmv = 1.0f / mv;
+    v.s2 = f16x2{(f16)p2, (f16)p2};
+    v.b2 = f16x2{(f16)(-1152.0f * p2), (f16)(-1152.0f * p2)};
+    return v;
+  }
+  static TM_DEV void stage_store(const Stage& r, int route, int tid, char* kl, char* vl,
+                                 f16x2 vs2 = f16x2{(f16)1.0f, (f16)1.0f},
+                                 f16x2 vb2 = f16x2{(f16)-1152.0f, (f16)-1152.0f}) {
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
       const int id = tid + 256 * i;
@@ -256,7 +282,7 @@ struct Attn {
         *reinterpret_cast<u32x4*>(kl + k16_off(R, 2 * col)) = c0;
         *reinterpret_cast<u32x4*>(kl + k16_off(R, 2 * col + 1)) = c1;
       }
-      i8x16_to_f16x16(r.v[i], c0, c1);
+      i8x16_to_f16x16(r.v[i], c0, c1, vs2, vb2);
       *reinterpret_cast<u32x4*>(vl + v_off(R, col * 16)) = c0;
       *reinterpret_cast<u32x4*>(vl + v_off(R, col * 16 + 8)) = c1;
     }
@@ -331,13 +357,12 @@ struct Attn {
   // take the reduction over the query's 4 lanes, move the reference and
   // rescale l and the accumulator (the same decision as reducing first, since
   // the reduced max exceeds the bound exactly when some lane's max does).
-  // Row sums: with an INT8 V cache each lane adds its p (before the v-scale)
-  // into lrow; with fp16 V the P.V step accumulates them on the MFMA into lacc
-  // (an all-ones A operand times P^T: every row of lacc holds the query's sum
-  // over the half's 32 keys), which takes the adds off the VALU.
+  // Row sums on the MFMA: an all-ones A operand times P^T gives, in every row,
+  // the query's sum over the half's 32 keys.  fp16 V accumulates it into lacc;
+  // INT8 V adds it, divided by the tile's mv, to lrow (see VSplit).
   // The reference max is kept negated (nref = -m_ref) so that every exponent
   // is one fma with it as the addend.
-  static TM_DEV void softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float vsc, float (&nref)[QB],
+  static TM_DEV void softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float lmv, float (&nref)[QB],
                              float (&lrow)[QB], f32x4 (&lacc)[QB], f32x4 (&O)[QB][NDB], f16x8 (&P)[QB]) {
     float lm[QB];
     bool up = false;
@@ -379,23 +404,17 @@ struct Attn {
       const f32x4 a = __builtin_bit_cast(f32x4, S[j][0]);
       const f32x4 b = __builtin_bit_cast(f32x4, S[j][1]);
       const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      float lsum = 0.0f;
+      // INT8 V: p mv = exp2(x c - m_ref + log2 mv)
+      const float add = KVI8 ? nref[j] + lmv : nref[j];
       u32x4 pk;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t], cj[j], nref[j]));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t + 1], cj[j], nref[j]));
-        f16x2 hv;
-        if (KVI8) {
-          hv = f16x2{(f16)(p0 * vsc), (f16)(p1 * vsc)};
-          lsum += p0 + p1;
-        } else {
-          hv = f16x2{(f16)p0, (f16)p1};
-        }
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t], cj[j], add));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * t + 1], cj[j], add));
+        const f16x2 hv = {(f16)p0, (f16)p1};
         pk[t] = __builtin_bit_cast(uint32_t, hv);
       }
       P[j] = __builtin_bit_cast(f16x8, pk);
-      if (KVI8) lrow[j] += lsum;
     }
   }
 
@@ -403,7 +422,7 @@ struct Attn {
   // keys 32h+4gq+0..3 (lo) and 32h+16+4gq+0..3 (hi); each comes from one
   // ds_read_b64_tr_b16 whose 16 lanes address 4 keys x 16 channels.
   static TM_DEV void pv(const char* vl, int h, const f16x8 (&P)[QB], f32x4 (&O)[QB][NDB], f32x4 (&lacc)[QB],
-                        int lane) {
+                        float (&lrow)[QB], float rmv, int lane) {
     const int gq = lane >> 4, jl = lane & 15;
     // key 32h + 16e + (4gq + jl/4), channels db*16 + 4*(jl%4) .. +3
     const char* base = vl + LV::lane(4 * gq + (jl >> 2)) + 8 * (jl & 3);
@@ -415,10 +434,15 @@ struct Attn {
 #pragma unroll
       for (int j = 0; j < QB; ++j) O[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, P[j], O[j][db], 0, 0, 0);
     }
-    if (!KVI8) {
-      const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+    const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
 #pragma unroll
-      for (int j = 0; j < QB; ++j) lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[j], lacc[j], 0, 0, 0);
+    for (int j = 0; j < QB; ++j) {
+      if (!KVI8) {
+        lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[j], lacc[j], 0, 0, 0);
+      } else {
+        const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[j], f32x4{0, 0, 0, 0}, 0, 0, 0);
+        lrow[j] = __builtin_fmaf(t[0], rmv, lrow[j]);
+      }
     }
   }
 };
@@ -594,17 +618,19 @@ void attn_prefill_kernel(const AttnArgs a) {
     typename A::Stage st;
     fetch(0, OTF ? 0 : (int)(wsh & 1), st, stA, false);
     if (KVI8 && !RAWST) {
+      const typename A::VSplit v0 = A::vsplit(vscale_row[0]);
       wait_vmem();
-      A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES);
+      A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, v0.s2, v0.b2);
     }
   }
   wait_vmem();
   if (OTF && (wsh & 1)) A::k_partial_amax(stA, wave, lane);
   __syncthreads();
   if (RAWST) {
+    const typename A::VSplit v0 = A::vsplit(vscale_row[0]);
     typename A::Stage st;
     A::stage_from_lds(st, tid, raw);
-    A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES);
+    A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, v0.s2, v0.b2);
     lds_barrier();
   }
 
@@ -677,7 +703,13 @@ void attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < QB; ++j) cj[j] = c16;
     }
-    const float vsc = KVI8 ? vscale_row[n] : 1.0f;
+    // INT8 V: this tile's scale split (mantissa into P, power of two into V)
+    float lmv = 0.0f, rmv = 1.0f;
+    if (KVI8) {
+      const typename A::VSplit vs = A::vsplit(vscale_row[n]);
+      lmv = vs.lmv;
+      rmv = vs.rmv;
+    }
     if (DBG) {
 #pragma unroll
       for (int j = 0; j < QB; ++j) {
@@ -720,14 +752,16 @@ void attn_prefill_kernel(const AttnArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
       f16x8 P[QB];
-      A::softmax(S, cj, vsc, nref, lrow, lacc, O, P);
+      A::softmax(S, cj, lmv, nref, lrow, lacc, O, P);
       __builtin_amdgcn_s_setprio(1);
-      A::pv(vl, h, P, O, lacc, lane);
+      A::pv(vl, h, P, O, lacc, lrow, rmv, lane);
       __builtin_amdgcn_s_setprio(0);
     }
     if (KVI8 && !RAWST) {
+      // (after the last tile the stage is stored but not read)
+      const typename A::VSplit vn = A::vsplit(last ? 1.0f : vscale_row[n + 1]);
       wait_vmem();
-      A::stage_store(st, rnext, tid, next, next + A::KBYTES);
+      A::stage_store(st, rnext, tid, next, next + A::KBYTES, vn.s2, vn.b2);
     }
     wait_vmem();
     // on-the-fly mode: this wave's max |k| of an INT8 next tile
@@ -736,9 +770,10 @@ void attn_prefill_kernel(const AttnArgs a) {
     // LDS staging: every wave is done with the stage and the raw next tile
     // has landed; widen it into the stage (skipped after the last tile)
     if (RAWST && !last) {
+      const typename A::VSplit vn = A::vsplit(vscale_row[n + 1]);
       typename A::Stage st;
       A::stage_from_lds(st, tid, raw);
-      A::stage_store(st, rnext, tid, next, next + A::KBYTES);
+      A::stage_store(st, rnext, tid, next, next + A::KBYTES, vn.s2, vn.b2);
       lds_barrier();
     }
     // next tile's group, in integer arithmetic (left >= 1; a compare here
@@ -767,8 +802,8 @@ void attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     if (j >= nh) continue;
-    // the row's sum: the lanes' partial sums (INT8 V), or any row of lacc
-    const float l = KVI8 ? rows4_sum(lrow[j]) : lacc[j][0];
+    // the row's sum (every lane of the query holds all of it)
+    const float l = KVI8 ? lrow[j] : lacc[j][0];
     const float inv = 1.0f / l;
     if (!qb_valid(j)) continue;
     // (row in tile) * Hq + (head in chunk)

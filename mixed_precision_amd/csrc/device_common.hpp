@@ -138,23 +138,26 @@ TM_DEV u32x2 quant8(const u32x4 v, float scale, float rs) {
   return u32x2{lo, hi};
 }
 
-// Four int8 (one dword) -> four fp16 (two dwords), exact: bias the bytes to
-// unsigned, splice them under the fp16 exponent of 1024 (bits 0x64uu encode
-// 1024 + u), then subtract 1152 with one packed fp16 add per pair.
-TM_DEV u32x2 i8x4_to_f16x4(uint32_t w) {
+// Four int8 (one dword) -> four fp16 (two dwords) times 2^E, exact: bias the
+// bytes to unsigned, splice them under the fp16 exponent of 1024 (bits 0x64uu
+// encode 1024 + u), then (1024 + u) 2^E - 1152 2^E = v 2^E in one packed fp16
+// fma per pair (scale = 2^E, bias = -1152 2^E, both exact in fp16 for E in
+// [-24, 5]; the fma's exact result v 2^E is a multiple of 2^-24 below 65504).
+TM_DEV u32x2 i8x4_to_f16x4(uint32_t w, f16x2 scale = f16x2{(f16)1.0f, (f16)1.0f},
+                           f16x2 bias = f16x2{(f16)-1152.0f, (f16)-1152.0f}) {
   const uint32_t t = w ^ 0x80808080u;
   const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u);
   const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u);
-  const f16x2 bias = {(f16)1152.0f, (f16)1152.0f};
-  const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
-  const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
+  const f16x2 a = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, lo), scale, bias);
+  const f16x2 b = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, hi), scale, bias);
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
-// Sixteen int8 -> two 16-byte chunks of fp16 (channels 0..7 and 8..15).
-TM_DEV void i8x16_to_f16x16(const u32x4 w, u32x4& c0, u32x4& c1) {
-  const u32x2 a = i8x4_to_f16x4(w.x), b = i8x4_to_f16x4(w.y);
-  const u32x2 c = i8x4_to_f16x4(w.z), d = i8x4_to_f16x4(w.w);
+// Sixteen int8 -> two 16-byte chunks of fp16 (channels 0..7 and 8..15), times 2^E.
+TM_DEV void i8x16_to_f16x16(const u32x4 w, u32x4& c0, u32x4& c1, f16x2 scale = f16x2{(f16)1.0f, (f16)1.0f},
+                            f16x2 bias = f16x2{(f16)-1152.0f, (f16)-1152.0f}) {
+  const u32x2 a = i8x4_to_f16x4(w.x, scale, bias), b = i8x4_to_f16x4(w.y, scale, bias);
+  const u32x2 c = i8x4_to_f16x4(w.z, scale, bias), d = i8x4_to_f16x4(w.w, scale, bias);
   c0 = u32x4{a.x, a.y, b.x, b.y};
   c1 = u32x4{c.x, c.y, d.x, d.y};
 }

@@ -772,3 +772,42 @@ def test_standard_config_full_size_sampled(gp, cfg, nsamp):
     ma, rf = max(errs), (num / den) ** 0.5
     print(f"  {w.name}: max_abs={ma:.3e} rel_fro={rf:.3e} over {len(errs)} tile rows")
     assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+@pytest.mark.parametrize("mode,nsamp", [("prefill", 24), ("decode", 64)])
+def test_chunked_bench_workloads_sampled(gp, mode, nsamp):
+    """The chunked-prefill and decode benchmark workloads at full size (512 new
+    tokens over 4096 cached keys, batch 8; one token over 4096 cached keys,
+    batch 64; 24/8 heads, d 128, INT8 cache, 75 % INT8), run as one call:
+    sampled query-tile rows and their log-sum-exp against the oracle."""
+    import torch
+    _announce(f"chunked bench workload {mode} sampled ({nsamp})")
+    if mode == "prefill":
+        w = make_chunked_workload(6, lengths_q=[512] * 8, lengths_k=[4096] * 8, num_q_heads=24, num_kv_heads=8,
+                                  head_dim=128, g=1, p=0.75, outliers=True, kv_int8=True)
+    else:
+        w = make_chunked_workload(7, lengths_q=[1] * 64, lengths_k=[4096] * 64, num_q_heads=24, num_kv_heads=8,
+                                  head_dim=128, g=1, p=0.75, outliers=True, kv_int8=True)
+    t = gp.prepare(w)
+    lse = torch.empty((w.q.shape[0], 24), dtype=torch.float32, device="cuda:0")
+    out = gp.attn(w, t, lse=lse)
+    torch.cuda.synchronize()
+    inp = oracle_inputs(w)
+    assert np.array_equal(gp.words_u64(t["words"]), inp.words)
+    got_all, lse_all = out.cpu().numpy(), lse.cpu().numpy()
+    rng = np.random.default_rng(61 if mode == "prefill" else 62)
+    errs, lerrs, num, den = [], [], 0.0, 0.0
+    for _ in range(nsamp):
+        b, hq = int(rng.integers(w.batch)), int(rng.integers(24))
+        s0, L = inp.spans[b]
+        m = int(rng.integers(orc.num_tiles(L)))
+        i0, i1 = m * 64, min(m * 64 + 64, L)
+        ref, ref_lse = orc.attn_tile_row(inp, b, hq, m, with_lse=True)
+        got = got_all[s0 + i0:s0 + i1, hq].astype(np.float64)
+        errs.append(np.max(np.abs(got - ref)))
+        lerrs.append(np.max(np.abs(lse_all[s0 + i0:s0 + i1, hq].astype(np.float64) - ref_lse)))
+        num += float(np.sum((got - ref) ** 2))
+        den += float(np.sum(ref ** 2))
+    ma, rf = max(errs), (num / den) ** 0.5
+    print(f"  {mode}: max_abs={ma:.3e} rel_fro={rf:.3e} lse={max(lerrs):.3e} over {nsamp} rows")
+    assert ma <= MAX_ABS and rf <= REL_FRO and max(lerrs) <= LSE_ABS
