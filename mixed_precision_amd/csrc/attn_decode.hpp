@@ -101,8 +101,9 @@ void attn_decode_kernel(const AttnArgs a) {
     typename A::Stage st;
     fetch(0, (int)(wsh & 1), st, stA, false);
     if (KVI8) {
+      const typename A::VSplit v0 = A::vsplit(vscale_row[0]);
       wait_vmem();
-      A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES);
+      A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, v0.s2, v0.b2);
     }
   }
   wait_vmem();
@@ -115,7 +116,14 @@ void attn_decode_kernel(const AttnArgs a) {
     typename A::Stage st;
     fetch(n + 1, rnext, st, next, last);
     const float ksc = kscale_row[n];
-    const float vsc = KVI8 ? vscale_row[n] : 1.0f;
+    // INT8 V: the tile's scale split as in the prefill kernel (the power of two
+    // widened into V, the mantissa into P, the row sum from the same fp16 P)
+    float lmv = 0.0f, rmv = 1.0f;
+    if (KVI8) {
+      const typename A::VSplit vs = A::vsplit(vscale_row[n]);
+      lmv = vs.lmv;
+      rmv = vs.rmv;
+    }
     // S^T for keys 64n + 16 wave + 4 gq + i of row c (raw: float bits or int32)
     i32x4 S;
     if (rc == 0) {
@@ -161,19 +169,17 @@ void attn_decode_kernel(const AttnArgs a) {
       // a wave whose keys so far are all masked (short caches) still has
       // m = -inf: its masked scores must give p = 0, not exp2(-inf + inf)
       const float mm = (mref == -INFINITY) ? 0.0f : mref;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[0], cj, -mm));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[1], cj, -mm));
-      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2], cj, -mm));
-      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[3], cj, -mm));
-      if (KVI8) {
-        P = f16x4{(f16)(p0 * vsc), (f16)(p1 * vsc), (f16)(p2 * vsc), (f16)(p3 * vsc)};
-        lsum += (p0 + p1) + (p2 + p3);
-      } else {
-        P = f16x4{(f16)p0, (f16)p1, (f16)p2, (f16)p3};
-        const f16x2 one = {(f16)1.0f, (f16)1.0f};
-        lsum = __builtin_amdgcn_fdot2(f16x2{P[0], P[1]}, one, lsum, false);
-        lsum = __builtin_amdgcn_fdot2(f16x2{P[2], P[3]}, one, lsum, false);
-      }
+      const float add = lmv - mm;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[0], cj, add));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[1], cj, add));
+      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2], cj, add));
+      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[3], cj, add));
+      P = f16x4{(f16)p0, (f16)p1, (f16)p2, (f16)p3};
+      // the wave's 16-key slice sum of P for the lane's query (all-ones A
+      // operand), divided by the INT8 V mantissa
+      const f16x4 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+      const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, P, f32x4{0, 0, 0, 0}, 0, 0, 0);
+      lsum = __builtin_fmaf(t[0], rmv, lsum);
     }
     // O^T += V^T P^T: lane (c, gq) reads channel db*16 + c of keys 16 wave + 4 gq .. +3
     const int jl = lane & 15;
@@ -182,8 +188,9 @@ void attn_decode_kernel(const AttnArgs a) {
     for (int db = 0; db < NDB; ++db)
       O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(read_tr16(vb + db * 32), P, O[db], 0, 0, 0);
     if (KVI8) {
+      const typename A::VSplit vn = A::vsplit(last ? 1.0f : vscale_row[n + 1]);
       wait_vmem();
-      A::stage_store(st, rnext, tid, next, next + A::KBYTES);
+      A::stage_store(st, rnext, tid, next, next + A::KBYTES, vn.s2, vn.b2);
     }
     wait_vmem();
     __syncthreads();
@@ -204,7 +211,7 @@ void attn_decode_kernel(const AttnArgs a) {
   // per row, M = max m_w, L = sum l_w 2^(m_w - M), acc = sum acc_w 2^(m_w - M)
   float* red = reinterpret_cast<float*>(stA);          // [4][16] m, then [4][16] l
   float* acc = reinterpret_cast<float*>(stB);          // [4][16 rows][D]
-  const float lrow = rows4_sum(lsum);
+  const float lrow = lsum;   // (every lane of the query holds the slice sum)
   if (gq == 0) {
     red[wave * 16 + c] = mref;
     red[64 + wave * 16 + c] = lrow;
