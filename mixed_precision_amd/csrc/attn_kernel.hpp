@@ -38,9 +38,11 @@
 //    registers); the next tile's loads are in flight while the current tile
 //    computes from the other half of a double-buffered stage.  K is fetched
 //    in the form its route needs (fp16 16 KB or int8 8 KB at d = 128).  An
-//    INT8 KV cache goes through registers, widened int8 -> fp16 exactly where
-//    the FP16 path or P.V needs it.  Buffer range checks return zeros past the
-//    sequence end, so ragged tails need no branches.
+//    INT8 KV cache is widened int8 -> fp16 exactly where the FP16 path or P.V
+//    needs it; the next tile waits in registers (up to 2 heads per item) or, as
+//    raw int8, in LDS (3 heads per item, whose q-blocks leave no room for the
+//    staging registers).  Buffer range checks return zeros past the sequence
+//    end, so ragged tails need no branches.
 //  * Scores live in the log2 domain: t = raw * c with c = sm_scale*log2(e)
 //    (FP16 path) or q_scale*k_scale*sm_scale*log2(e) (INT8 path), so both paths
 //    meet in one running max and p = exp2(raw*c - m) is one FMA plus v_exp_f32.
@@ -58,10 +60,14 @@
 //    of its own; one LDS-only barrier separates the quantised tile from its use.
 //    Scales and int8 values equal those of the quantise-once kernel bit for bit,
 //    so both modes give the same output.
-//  * With an fp16 V the normaliser l sums the fp16-rounded probabilities that
-//    actually enter P.V (v_dot2_f32_f16), so O is an exact weighted mean of V
-//    rows with slightly perturbed weights and the dominant term's rounding
-//    cancels.
+//  * The normaliser l sums the fp16-rounded probabilities that actually enter
+//    P.V, on the MFMA (an all-ones A operand times P^T), so O is an exact
+//    weighted mean of V rows with slightly perturbed weights and the dominant
+//    term's rounding cancels.  With an INT8 V the v scale's power of two is
+//    widened into V exactly and its mantissa enters P (see VSplit).
+//  * The kernel is bound by the SIMD's VALU issue port, which the MFMAs share
+//    (each 16x16x32 f16 MFMA takes about 7 cycles of the other wave's VALU
+//    issue); the softmax is written for the fewest VALU instructions per score.
 #pragma once
 #include "device_common.hpp"
 #include "internal.hpp"
