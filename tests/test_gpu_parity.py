@@ -811,3 +811,30 @@ def test_chunked_bench_workloads_sampled(gp, mode, nsamp):
     ma, rf = max(errs), (num / den) ** 0.5
     print(f"  {mode}: max_abs={ma:.3e} rel_fro={rf:.3e} lse={max(lerrs):.3e} over {nsamp} rows")
     assert ma <= MAX_ABS and rf <= REL_FRO and max(lerrs) <= LSE_ABS
+
+
+def test_attn_strided_layouts_bitexact(gp):
+    """Addressing only: the same operands in other memory layouts give the same
+    bits.  Q, K and V as views into one packed QKV buffer (token stride
+    (Hq + 2 Hk) d); an INT8 KV cache stored head-major ([Hk][N][d] viewed as
+    [N][Hk][d]) for chunked prefill and for decode."""
+    import torch
+    _announce("attn strided layouts")
+    w = make_workload(538, lengths=[200, 64, 130, 1], num_q_heads=6, num_kv_heads=2, head_dim=128, g=1, p=0.6,
+                      outliers=True)
+    t = gp.prepare(w)
+    ref = gp.attn(w, t).clone()
+    N = int(w.cu_seqlens[-1])
+    qkv = torch.empty((N, 10, 128), dtype=torch.float16, device="cuda:0")
+    qkv[:, :6], qkv[:, 6:8], qkv[:, 8:] = t["q"], t["k"], t["v"]
+    t2 = dict(t, q=qkv[:, :6], k=qkv[:, 6:8], v=qkv[:, 8:])
+    assert torch.equal(gp.attn(w, t2), ref)
+    for seed, lq, lk in ((539, [130, 64, 7], [900, 64, 300]), (540, [1] * 9, [1, 63, 64, 65, 200, 511, 1000, 2049, 3000])):
+        w = make_chunked_workload(seed, lengths_q=lq, lengths_k=lk, num_q_heads=6, num_kv_heads=2, head_dim=128, g=1,
+                                  p=0.6, outliers=True, kv_int8=True)
+        t = gp.prepare(w)
+        ref = gp.attn(w, t).clone()
+        head_major = lambda x: x.transpose(0, 1).contiguous().transpose(0, 1)
+        t2 = dict(t, k8=head_major(t["k8"]), v8=head_major(t["v8"]))
+        assert t2["k8"].stride(0) == 128 and t2["k8"].stride(1) == int(w.cu_seqlens_k[-1]) * 128
+        assert torch.equal(gp.attn(w, t2), ref)
