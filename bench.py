@@ -328,8 +328,9 @@ def main():
                     help="only copy MIB MiB device to device a few times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
-              "the sharding design is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the path has no multi-GPU mode (it would "
+              "shard by KV head, each GPU taking its heads' K/V, route words and query heads, with no exchange)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -16,8 +16,8 @@ products in exact int64) of what the method computes, written from the pages:
   [GS]     gist.science technical summary (Spanish), "Resumen Tecnico", subsection
            "Enrutamiento por Mascara de Bits Compacta".
 
-Readings taken where the pages leave a step open are listed in the design doc
-("Readings of the pages") and restated at each function.
+Readings taken where the pages leave a step open are restated at each
+function that takes them.
 
 Conventions (all readings):
   * score tiles are 64 x 64 (BLOCK_M = BLOCK_N = 64);
