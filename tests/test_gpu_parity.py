@@ -514,6 +514,9 @@ CHUNKED = [
     ("decode_gqa3_d64_int8kv", [1] * 3, [2, 333, 4097], 6, 2, 64, 2, 0.5, True, 64),
     # chunked prefill, INT8 cache, GQA 3 (three heads per item, LDS staging)
     ("chunk_int8kv_gqa3", [190, 64, 5], [900, 64, 700], 6, 2, 128, 1, 0.5, True, 64),
+    # decode with more query heads per KV head than one 16-row block: the fused
+    # prefill kernel takes it (7 items of 3 heads, one query row each)
+    ("decode_gqa20_int8kv", [1] * 3, [5, 640, 2500], 20, 1, 128, 2, 0.5, True, 64),
 ]
 
 
