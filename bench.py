@@ -380,27 +380,23 @@ def main():
     work = work_model(w, words.cpu().numpy().view(np.uint64))
 
     # The route words and the work list depend only on the routing template and
-    # cu_seqlens: they are built on a second stream while the quantiser streams Q
-    # on the main stream and K (and V) on a third; the attention waits for all.
-    # Every stream has the default priority.
+    # cu_seqlens: they are built on a second stream (default priority) while the
+    # quantiser streams Q and K, and the attention waits for both.  (Quantising K
+    # on a third stream beside Q measured no faster: both are HBM-bound, and each
+    # cross-stream wait costs several microseconds.)
     side = torch.cuda.Stream(device=dev)
-    kvs = torch.cuda.Stream(device=dev)
 
     def step(ev=None, stream=stream):
         side.wait_stream(stream)                 # the previous step's attention has read words / work list
-        kvs.wait_stream(stream)                  # ... and K8 / V8
         with torch.cuda.stream(side):
             tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=side)
             plan.schedule(cu, stream=side)
-        with torch.cuda.stream(kvs):
-            if not args.otf:
-                tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=kvs)
-            if w.kv_int8:
-                tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=kvs)
         if not args.otf:
             tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
+            tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
+        if w.kv_int8:
+            tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
         stream.wait_stream(side)
-        stream.wait_stream(kvs)
         if ev is not None:
             ev[0].record(stream)
         if w.kv_int8:
@@ -425,8 +421,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     eager_ms = ms_per_step
     if args.graph:
-        # the same step captured once in a HIP graph (three streams forked from
-        # and joined to the capture stream) and replayed
+        # the same step captured once in a HIP graph (the side stream forked
+        # from and joined to the capture stream) and replayed
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(stream=torch.cuda.current_stream())
