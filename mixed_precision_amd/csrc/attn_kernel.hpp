@@ -106,9 +106,10 @@ template <int D, int QB, bool KVI8>
 struct Attn {
   // The reference max may lag the true running max by up to kSlack (log2
   // units), so p <= 2^kSlack.  FP16 V: p itself must stay finite in fp16
-  // (2^15 < 65504).  INT8 V: p * v_scale goes to fp16, so 2^8 keeps it finite
-  // for any |V| below 32,500 (v_scale < 256).
-  static constexpr float kSlack = KVI8 ? 8.0f : 15.0f;
+  // (2^15 < 65504).  INT8 V: P = p mv carries the v scale's mantissa mv
+  // (VSplit), below 16.2 for any scale of fp16 data (s_v <= 65504 / 127), so
+  // 2^11 keeps P below 2^15.
+  static constexpr float kSlack = KVI8 ? 11.0f : 15.0f;
   // When the reference moves, FP16 V sets it kOver above the new maximum, so
   // the row's maximum can grow by kOver + kSlack before the next rescale
   // (fewer O rescales on rows whose maximum keeps rising).  The largest p is
@@ -116,7 +117,7 @@ struct Attn {
   // full precision, and the smaller ones fall into its subnormal range, whose
   // absolute step is 2^-24.  With near one-hot rows (outlier channels) an
   // overshoot of 8 doubled the worst output error; 4 left it unchanged.
-  static constexpr float kOver = KVI8 ? 0.0f : 4.0f;
+  static constexpr float kOver = 4.0f;
   static constexpr int NDS = D / 32;       // fp16 MFMA k-steps over d
   static constexpr int NDS8 = D / 64;      // int8 MFMA k-steps over d
   static constexpr int NDB = D / 16;       // 16-row blocks of d in O^T
