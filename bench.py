@@ -302,8 +302,8 @@ def chunked_bench(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--p", type=float, default=None, help="INT8 coverage override (configs 2, 4, 5)")
     ap.add_argument("--otf", action="store_true",
