@@ -32,19 +32,32 @@ P_INT8 = 5033.2e12        # OP/s
 HBM_PEAK = 8.0e12         # B/s
 
 
+# what decides the attention kernel's code on this workload: its header, the
+# file that instantiates it at 3 heads per work item, and the build flags
+KERNEL_SOURCES = ("mixed_precision_amd/csrc/attn_kernel.hpp", "mixed_precision_amd/csrc/attn_d128_qb3.hip",
+                  "mixed_precision_amd/build.py")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload_name):
     """HBM bytes per attention launch from the committed counter summary, if it was taken on this
-    workload with the attention kernel source as it is now (else None)."""
-    import hashlib
+    workload with the attention kernel sources as they are now (else None)."""
     import re
     prof = os.path.join(ROOT, "profiles", "attn_prefill_kernel_llama3b_B8_L4096_hbm_bytes.md")
-    src = os.path.join(ROOT, "mixed_precision_amd", "csrc", "attn_kernel.hpp")
     if workload_name != "llama3.2-3b_attn_B8_L4096_h24kv8_d128_int8p75" or not os.path.exists(prof):
         return None
     text = open(prof).read()
-    h = re.search(r"source sha256: `([0-9a-f]{64})`", text)
+    h = re.search(r"sources sha256[^:]*: `([0-9a-f]{64})`", text)
     t = re.search(r"roofline.traffic` = (\d+) bytes", text)
-    if not h or not t or h.group(1) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if not h or not t or h.group(1) != kernel_source_digest():
         return None
     return int(t.group(1))
 

@@ -30,6 +30,12 @@ CXXFLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ] + os.environ.get("TILEMIX_EXTRA_FLAGS", "").split()
 
+# flags for single sources: the 3-heads-per-item attention kernels schedule
+# for instruction-level parallelism (measured faster there; slower at 2 heads)
+SOURCE_FLAGS = {
+    "attn_d128_qb3.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -44,7 +50,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + CXXFLAGS + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + CXXFLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
