@@ -377,6 +377,44 @@ def test_attn_zero_scale_blocks(gp):
     assert ma <= MAX_ABS and rf <= REL_FRO
 
 
+@pytest.mark.parametrize("case", ["large_scales", "tiny_key_tiles"])
+def test_attn_int8_score_scale_extremes(gp, case):
+    """INT8 score factors at both ends.  large_scales: Q and K scaled so that
+    s_q s_k sm log2(e) >= 1/2 on every tile (near one-hot rows, scores of
+    thousands of log2 units).  tiny_key_tiles: every other key tile scaled by
+    1e-4, so rows reach those tiles with a reference maximum far above their
+    scores.  Output against the oracle, quantise-once and on-the-fly."""
+    import torch
+    _announce(f"attn INT8 score scales {case}")
+    if case == "large_scales":
+        w = make_workload(475, lengths=[300, 150], num_q_heads=3, num_kv_heads=1, head_dim=128, g=1,
+                          route="ones", p=1.0)
+        w.q *= np.float16(100.0)
+        w.k *= np.float16(100.0)
+    else:
+        w = make_workload(476, lengths=[400, 200], num_q_heads=6, num_kv_heads=2, head_dim=128, g=1, p=0.5,
+                          outliers=True)
+        for b, (s0, L) in enumerate(orc.seq_spans(w.cu_seqlens)):
+            for n in range(1, (L + 63) // 64, 2):
+                w.k[s0 + 64 * n:s0 + min(64 * n + 64, L)] *= np.float16(1e-4)
+    t = gp.prepare(w)
+    if case == "large_scales":
+        inp = oracle_inputs(w)
+        qs, ks = inp.q_scale.astype(np.float64), inp.k_scale.astype(np.float64)   # (unused blocks hold 0)
+        c = (qs[qs > 0].min() * ks[ks > 0].min()
+             * float(w.sm_scale) * 1.4426950408889634)
+        assert c >= 0.5
+    ref = orc.attn_prefill(oracle_inputs(w))
+    for otf in (False, True):
+        out = gp.attn(w, t, out_fp32=True, otf=otf)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.all(np.isfinite(got))
+        ma, rf = gp.errors(got, ref)
+        print(f"  otf={otf} max_abs={ma:.3e} rel_fro={rf:.3e}")
+        assert ma <= MAX_ABS and rf <= REL_FRO
+
+
 def test_attn_plan_then_run_equals_prefill(gp):
     """tilemix_attn_plan + tilemix_attn_run give the same bits as tilemix_attn_prefill,
     and one plan serves repeated runs."""
