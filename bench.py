@@ -4,8 +4,12 @@ A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: blockwise INT8 quantisation of Q and K (and V for the
 INT8 KV cache), route-word packing, the varlen/GQA work list and the fused
 attention kernel (packing and the work list run on a second stream beside the
-quantiser).  With --otf the quantiser calls drop out and the attention
-kernel makes the INT8 operands on chip.  Default workload: the LLaMA-3.2-3B-shaped attention layer
+quantiser).  For an fp16 K/V the attention kernel makes Q's INT8 operands
+on chip by default, so the step's quantiser call covers K only; --once
+quantises Q beforehand as well, --otf makes K's on chip too.  All three give
+the same output bits.  The step is captured once as a HIP graph and replayed
+(--eager: launched directly); the attention kernel's own time comes from HIP
+events around it in the eager steps that precede the capture.  Default workload: the LLaMA-3.2-3B-shaped attention layer
 (batch 8, L = 4096, 24 query / 8 KV heads, d = 128, causal, FP16, 4 outlier
 channels, 64x64 tiles, g = 1, 75 % of the legal tile groups INT8).
 
@@ -322,6 +326,9 @@ def main():
     ap.add_argument("--otf", action="store_true",
                     help="on-the-fly quantisation: Q/K INT8 operands made inside the attention kernel "
                          "(no quantiser calls in the step)")
+    ap.add_argument("--once", action="store_true",
+                    help="quantise-once operands: the step quantises Q and K before the attention kernel "
+                         "(default for an fp16 K/V: Q's operands made inside the kernel, K quantised once)")
     ap.add_argument("--deviation-sweep", type=str, default=None, metavar="P,P,...",
                     help="instead of the bench line: MaxDiff / MeanDiff of the routed output against the "
                          "0 %% INT8 output at each INT8 coverage (Bernoulli-routed workloads), one JSON line each")
@@ -333,13 +340,15 @@ def main():
                          "or decode (1 new token over 4096 cached, batch 64) on an INT8 KV cache")
     ap.add_argument("--kv-layout", choices=["token", "head"], default="token",
                     help="with --chunked: INT8 cache stored token-major [N][Hk][d] or head-major [Hk][N][d]")
-    ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph (attention times "
-                    "still come from the eager steps' events)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the step directly instead of replaying it as a captured HIP graph")
+    ap.add_argument("--graph", action="store_true", help="(the default) replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device a few times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
+    args.graph = not args.eager
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the path has no multi-GPU mode (it would "
               "shard by KV head, each GPU taking its heads' K/V, route words and query heads, with no exchange)",
@@ -373,8 +382,13 @@ def main():
     if args.otf and w.kv_int8:
         print("--otf applies to an fp16 K/V workload", file=sys.stderr)
         sys.exit(2)
+    if args.otf and args.once:
+        print("--otf and --once are exclusive", file=sys.stderr)
+        sys.exit(2)
+    # operand preparation (otf_quant): 0 quantise-once, 1 Q and K on chip, 2 Q on chip
+    mode = 1 if args.otf else (0 if (args.once or w.kv_int8) else 2)
     plan = tm.AttnPlan(tm.AttnProblem(B, w.max_seqlen, Hq, Hk, d, w.g, w.blk_q, w.sm_scale, w.kv_int8, False,
-                                      args.otf), dev)
+                                      mode), dev)
     nbq = (w.max_seqlen + w.blk_q - 1) // w.blk_q
     T = w.T
     q_q = torch.empty((N, Hq, d), dtype=torch.int8, device=dev)
@@ -404,8 +418,9 @@ def main():
         with torch.cuda.stream(side):
             tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=side)
             plan.schedule(cu, stream=side)
-        if not args.otf:
+        if mode == 0:
             tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
+        if mode != 1:
             tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
         if w.kv_int8:
             tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
@@ -414,8 +429,10 @@ def main():
             ev[0].record(stream)
         if w.kv_int8:
             plan.run_planned(q, k_q, v_q, q_q, q_s, None, k_s, cu, words, out, v_scale=v_s, stream=stream)
-        elif args.otf:
+        elif mode == 1:
             plan.run_planned(q, k, v, None, None, None, None, cu, words, out, stream=stream)
+        elif mode == 2:
+            plan.run_planned(q, k, v, None, None, k_q, k_s, cu, words, out, stream=stream)
         else:
             plan.run_planned(q, k, v, q_q, q_s, k_q, k_s, cu, words, out, stream=stream)
         if ev is not None:
@@ -459,10 +476,11 @@ def main():
         "dtype": "fp16+int8 (fp32 accumulation / int32 accumulation)", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": w.max_seqlen, "num_q_heads": Hq, "num_kv_heads": Hk,
                    "head_dim": d, "g": w.g, "blk_q": w.blk_q, "kv_int8": w.kv_int8,
-                   "operands": "on-the-fly" if args.otf else "quantize-once",
+                   "operands": ("quantize-once", "on-the-fly", "on-the-fly Q")[mode],
                    "int8_pair_fraction": work["pairs_int8"] / work["pairs"], "tokens": N},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / blended_peak, "traffic": None if args.otf else measured_traffic(w.name),
+                     "frac": achieved / blended_peak,
+                     "traffic": measured_traffic(w.name) if mode == 2 else None,
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "kernel": "attn_prefill_kernel",
                      "note": "peak = blended MFMA peak of this launch's mix: ops / (F_qk16/P16 + F_qk8/P8 + F_pv/P16)"},

@@ -182,7 +182,11 @@ typedef struct {
                            and INT8 fragments of Q and of INT8-routed K tiles on chip from
                            q and k, with the same definition and bit-identical results;
                            q_q, q_scale, k_q and k_scale are not read (may be NULL).
-                           Requires kv_int8 = 0. */
+                           2: on-the-fly Q only: Q's block scales and INT8 fragments are
+                           made on chip as in 1 (q_q and q_scale are not read), and K
+                           takes the quantise-once k_q and k_scale.  Same results as 0
+                           and 1, bit for bit; saves the separate pass over Q.
+                           1 and 2 require kv_int8 = 0. */
   int32_t max_seqlen_k; /* 0: prefill, the keys are the queries' positions.  > 0: chunked
                            prefill / decode over a KV cache (an extension: the pages scope
                            the method to prefill, [PL Limitations], and list decode as not
@@ -200,8 +204,8 @@ typedef struct {
   int64_t q_stride_tok, q_stride_head;    /* elements; multiples of 8; 16-byte aligned base */
   int64_t kv_stride_tok, kv_stride_head;  /* elements; multiples of 8 (fp16) or 16 (int8) */
   const int8_t* q_q;      /* int8 [N][Hq][d] contiguous, from tilemix_quantize_blockwise(q, blk_q);
-                             unused when otf_quant = 1 */
-  const float* q_scale;   /* float32 [Hq][batch][ceil(max_seqlen/blk_q)]; unused when otf_quant = 1 */
+                             unused when otf_quant = 1 or 2 */
+  const float* q_scale;   /* float32 [Hq][batch][ceil(max_seqlen/blk_q)]; unused when otf_quant = 1 or 2 */
   const int8_t* k_q;      /* kv_int8 = 0: int8 [N][Hk][d] contiguous (quantize_blockwise(k, 64));
                              unused when kv_int8 = 1 or otf_quant = 1 */
   const float* k_scale;   /* float32 [Hk][batch][Tk]: per 64-token block of K; unused when otf_quant = 1 */
@@ -230,7 +234,8 @@ int32_t tilemix_attn_workspace_size(const tilemix_attn_params* params, size_t* b
  *                  kv_int8 = 1 uses k = k_int8 * k_scale exactly)
  *   R = 1 (INT8):  s_ij = sm_scale * q_scale(i) * k_scale(j) * S32_ij,
  *                  S32 = int8 MFMA with exact int32 accumulation of q_q . k_q
- *                  (otf_quant = 1: q_q, k_q and their scales are made on chip)
+ *                  (otf_quant = 1: q_q, k_q and their scales are made on chip;
+ *                  otf_quant = 2: q_q and q_scale)
  * Both paths update one online-softmax state per query row (running max, sum
  * and output accumulator in fp32); P.V runs in fp16 with fp32 accumulation
  * (kv_int8 = 1: v = v_int8 * v_scale, the scale folded into P); the output is

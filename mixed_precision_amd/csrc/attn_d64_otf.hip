@@ -1,17 +1,28 @@
 // Instantiations of the fused attention kernel for head_dim 64, FP16 K/V, with
-// Q and K quantised on the fly inside the kernel.
+// Q and K, or Q alone, quantised on the fly inside the kernel.
 #include "attn_kernel.hpp"
 
 namespace tilemix {
 
 hipError_t launch_attn_d64_otf(const AttnArgs& a, int64_t nslots, bool debug, hipStream_t s) {
+  if (a.otf == kOtfQ) {
+    switch (a.hc * 2 + (debug ? 1 : 0)) {
+      case 2: return launch_attn_inst<64, 1, false, kOtfQ, false>(a, nslots, s);
+      case 3: return launch_attn_inst<64, 1, false, kOtfQ, true>(a, nslots, s);
+      case 4: return launch_attn_inst<64, 2, false, kOtfQ, false>(a, nslots, s);
+      case 5: return launch_attn_inst<64, 2, false, kOtfQ, true>(a, nslots, s);
+      case 6: return launch_attn_inst<64, 3, false, kOtfQ, false>(a, nslots, s);
+      case 7: return launch_attn_inst<64, 3, false, kOtfQ, true>(a, nslots, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.hc * 2 + (debug ? 1 : 0)) {
-    case 2: return launch_attn_inst<64, 1, false, true, false>(a, nslots, s);
-    case 3: return launch_attn_inst<64, 1, false, true, true>(a, nslots, s);
-    case 4: return launch_attn_inst<64, 2, false, true, false>(a, nslots, s);
-    case 5: return launch_attn_inst<64, 2, false, true, true>(a, nslots, s);
-    case 6: return launch_attn_inst<64, 3, false, true, false>(a, nslots, s);
-    case 7: return launch_attn_inst<64, 3, false, true, true>(a, nslots, s);
+    case 2: return launch_attn_inst<64, 1, false, kOtfQK, false>(a, nslots, s);
+    case 3: return launch_attn_inst<64, 1, false, kOtfQK, true>(a, nslots, s);
+    case 4: return launch_attn_inst<64, 2, false, kOtfQK, false>(a, nslots, s);
+    case 5: return launch_attn_inst<64, 2, false, kOtfQK, true>(a, nslots, s);
+    case 6: return launch_attn_inst<64, 3, false, kOtfQK, false>(a, nslots, s);
+    case 7: return launch_attn_inst<64, 3, false, kOtfQK, true>(a, nslots, s);
     default: return hipErrorInvalidValue;
   }
 }

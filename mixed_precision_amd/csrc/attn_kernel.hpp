@@ -59,7 +59,9 @@
 //    their max |k| before the end-of-tile barrier, so the scale costs no barrier
 //    of its own; one LDS-only barrier separates the quantised tile from its use.
 //    Scales and int8 values equal those of the quantise-once kernel bit for bit,
-//    so both modes give the same output.
+//    so both modes give the same output.  The Q-only variant makes Q's operands
+//    the same way and takes K quantised once: it saves the step's Q pass (Q is
+//    read here anyway) without quantising a K tile once per query tile.
 //  * The normaliser l sums the fp16-rounded probabilities that actually enter
 //    P.V, on the MFMA (an all-ones A operand times P^T), so O is an exact
 //    weighted mean of V rows with slightly perturbed weights and the dominant
@@ -454,9 +456,15 @@ struct Attn {
   }
 };
 
-template <int D, int QB, bool KVI8, bool OTF, bool DBG>
+// Operand preparation of the prefill kernel: Q and K quantised beforehand, both
+// quantised in the kernel, or Q in the kernel and K beforehand.
+enum OtfMode : int { kOtfNone = 0, kOtfQK = 1, kOtfQ = 2 };
+
+template <int D, int QB, bool KVI8, int OTFM, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_kernel(const AttnArgs a) {
+  constexpr bool OTF = OTFM == kOtfQK;    // K (and Q) quantised in the kernel
+  constexpr bool QOTF = OTFM != kOtfNone; // Q quantised in the kernel
   static_assert(!(KVI8 && OTF), "on-the-fly quantisation applies to an fp16 K");
   using A = Attn<D, QB, KVI8>;
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
@@ -476,7 +484,7 @@ void attn_prefill_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char raw[RAWST ? A::RAW_BYTES : 16];
   // on-the-fly mode: the current INT8 tile's K, and per-wave Q-block maxima
   __shared__ __attribute__((aligned(16))) char k8s[OTF ? A::L8::BYTES : 16];
-  __shared__ uint32_t qam[OTF ? 3 * 4 : 1];
+  __shared__ uint32_t qam[QOTF ? 3 * 4 : 1];
 
   const WorkItem item = a.items[blockIdx.x];
   const int b = uniform(item.b);
@@ -513,7 +521,7 @@ void attn_prefill_kernel(const AttnArgs a) {
   // into NaN; scales made by the quantiser are far above that floor.
   constexpr float kScaleFloor = 1.0842022e-19f;
   float sqs[QB];
-  if (!OTF) {
+  if (!QOTF) {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const int blk_start = m * kTile + qb_rb(j) * 16;
@@ -538,16 +546,30 @@ void attn_prefill_kernel(const AttnArgs a) {
       qf[j][ds] = valid ? *reinterpret_cast<const f16x8*>(qptr + tok * a.q_st + (int64_t)hqj * a.q_sh + ds * 32 +
                                                          gq * 8)
                         : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (!OTF) {
+    if (!QOTF) {
 #pragma unroll
       for (int ds = 0; ds < NDS8; ++ds)
         q8[j][ds] = valid ? *reinterpret_cast<const i32x4*>(a.q_q + (tok * a.Hq + hqj) * D + ds * 64 + gq * 16)
                           : i32x4{0, 0, 0, 0};
     }
   }
-  // on-the-fly mode: max |q| over the Q block (blk_q rows of the sequence,
-  // all channels) of every head of the chunk, one partial per wave
-  if (OTF) {
+  // on-the-fly Q: max |q| over the Q block (blk_q rows of the sequence,
+  // all channels) of every head of the chunk, four partials per head.  A
+  // 64-row block is this item's query tile, whose rows the waves hold in qf:
+  // one partial per q-block (16 rows); a 128-row block is read again, one
+  // partial per wave.
+  if (QOTF && a.blk_q == kTile) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      if (j < nh) {
+        u16x2 mx = {0, 0};
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) mx = absmax_acc(mx, __builtin_bit_cast(u32x4, qf[j][ds]));
+        const uint32_t am = wave_max_u32(absmax_bits(mx));
+        if (lane == 0) qam[wave * nh + j] = am;   // = head * 4 + row block
+      }
+    }
+  } else if (QOTF) {
     constexpr int CPR = D / 8;   // 16-byte chunks per row
     const int qb0 = (m * kTile / a.blk_q) * a.blk_q;
     const int qrows = min(a.blk_q, L - qb0);
@@ -641,9 +663,9 @@ void attn_prefill_kernel(const AttnArgs a) {
     lds_barrier();
   }
 
-  // on-the-fly mode: Q block scales and the INT8 Q operands (channels
+  // on-the-fly Q: Q block scales and the INT8 Q operands (channels
   // 64 ds + 16 gq .. +15 of the lane's query row)
-  if (OTF) {
+  if (QOTF) {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       float sq = 1.0f;
@@ -832,9 +854,9 @@ void attn_prefill_kernel(const AttnArgs a) {
   }
 }
 
-template <int D, int QB, bool KVI8, bool OTF, bool DBG>
+template <int D, int QB, bool KVI8, int OTFM, bool DBG>
 hipError_t launch_attn_inst(const AttnArgs& a, int64_t nslots, hipStream_t s) {
-  hipLaunchKernelGGL((attn_prefill_kernel<D, QB, KVI8, OTF, DBG>), dim3((unsigned)nslots), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_prefill_kernel<D, QB, KVI8, OTFM, DBG>), dim3((unsigned)nslots), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

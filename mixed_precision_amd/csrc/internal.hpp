@@ -72,7 +72,8 @@ struct AttnArgs {
   float sm_log2;     // fl32(sm_scale * log2(e))
   int32_t out_fp32;
   int32_t kv_int8;
-  int32_t otf;       // Q and K quantised inside the kernel (q_q, q_scale, k_q, k_scale unused)
+  int32_t otf;       // 1: Q and K quantised inside the kernel (q_q, q_scale, k_q, k_scale unused);
+                     // 2: Q alone (q_q, q_scale unused)
   // debug products (fused kernel with DBG = true only)
   int32_t dbg_seq, dbg_head, dbg_m0, dbg_m1;
   int32_t* dbg_s32;

@@ -86,9 +86,9 @@ int32_t validate_attn_params(const tilemix_attn_params* p) {
   if (p->causal != 1) return fail(TILEMIX_ERR_UNSUPPORTED, "causal = %d: only causal prefill is implemented", p->causal);
   if (p->kv_int8 != 0 && p->kv_int8 != 1) return fail(TILEMIX_ERR_INVALID_ARG, "kv_int8 must be 0 or 1");
   if (p->out_fp32 != 0 && p->out_fp32 != 1) return fail(TILEMIX_ERR_INVALID_ARG, "out_fp32 must be 0 or 1");
-  if (p->otf_quant != 0 && p->otf_quant != 1) return fail(TILEMIX_ERR_INVALID_ARG, "otf_quant must be 0 or 1");
+  if (p->otf_quant < 0 || p->otf_quant > 2) return fail(TILEMIX_ERR_INVALID_ARG, "otf_quant must be 0, 1 or 2");
   if (p->otf_quant && p->kv_int8)
-    return fail(TILEMIX_ERR_UNSUPPORTED, "otf_quant = 1 quantises an fp16 K: it cannot be combined with kv_int8 = 1");
+    return fail(TILEMIX_ERR_UNSUPPORTED, "otf_quant = %d cannot be combined with kv_int8 = 1", p->otf_quant);
   if (p->max_seqlen_k < 0) return fail(TILEMIX_ERR_INVALID_ARG, "max_seqlen_k %d must be >= 0", p->max_seqlen_k);
   if (p->max_seqlen_k > 0 && p->max_seqlen_k < p->max_seqlen)
     return fail(TILEMIX_ERR_INVALID_ARG, "max_seqlen_k %d < max_seqlen %d: a chunk has no more queries than keys",
@@ -126,8 +126,9 @@ Derived derive(const tilemix_attn_params* p) {
 int32_t validate_tensors(const tilemix_attn_params* p, const tilemix_attn_tensors* t) {
   if (!t) return fail(TILEMIX_ERR_INVALID_ARG, "tensors is NULL");
   if (!t->q || !t->k || !t->v) return fail(TILEMIX_ERR_INVALID_ARG, "q, k and v must be non-NULL");
-  const bool otf = p->otf_quant != 0;
-  if (!otf && (!t->q_q || !t->q_scale)) return fail(TILEMIX_ERR_INVALID_ARG, "q_q and q_scale must be non-NULL");
+  const bool otf = p->otf_quant == 1;              // Q and K made on chip
+  const bool qotf = p->otf_quant != 0;             // Q made on chip
+  if (!qotf && (!t->q_q || !t->q_scale)) return fail(TILEMIX_ERR_INVALID_ARG, "q_q and q_scale must be non-NULL");
   if (!otf && !t->k_scale) return fail(TILEMIX_ERR_INVALID_ARG, "k_scale must be non-NULL");
   if (!otf && !p->kv_int8 && !t->k_q)
     return fail(TILEMIX_ERR_INVALID_ARG, "k_q must be non-NULL when kv_int8 = 0");
@@ -138,10 +139,10 @@ int32_t validate_tensors(const tilemix_attn_params* p, const tilemix_attn_tensor
     return fail(TILEMIX_ERR_INVALID_ARG, "cu_seqlens_k must be given exactly when max_seqlen_k > 0 (chunked prefill)");
   if ((t->cu_seqlens_k && !aligned(t->cu_seqlens_k, 4)) || (t->lse && !aligned(t->lse, 4)))
     return fail(TILEMIX_ERR_INVALID_ARG, "misaligned cu_seqlens_k or lse pointer");
-  if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16) || (!otf && !aligned(t->q_q, 16)) ||
+  if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16) || (!qotf && !aligned(t->q_q, 16)) ||
       (!otf && t->k_q && !aligned(t->k_q, 16)) || !aligned(t->out, 16))
     return fail(TILEMIX_ERR_INVALID_ARG, "q, k, v, q_q, k_q and out must be 16-byte aligned");
-  if (!aligned(t->route_words, 8) || (!otf && (!aligned(t->q_scale, 4) || !aligned(t->k_scale, 4))) ||
+  if (!aligned(t->route_words, 8) || (!qotf && !aligned(t->q_scale, 4)) || (!otf && !aligned(t->k_scale, 4)) ||
       !aligned(t->cu_seqlens, 4) || (t->v_scale && !aligned(t->v_scale, 4)))
     return fail(TILEMIX_ERR_INVALID_ARG, "misaligned scale, cu_seqlens or route_words pointer");
   const int64_t kv_mult = p->kv_int8 ? 16 : 8;
@@ -259,9 +260,11 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
   a.out_fp32 = p->out_fp32;
   a.kv_int8 = p->kv_int8;
   a.otf = p->otf_quant;
-  if (a.otf) {   // not read in this mode
+  if (a.otf) {   // not read in these modes
     a.q_q = nullptr;
     a.q_scale = nullptr;
+  }
+  if (a.otf == 1) {
     a.k_q = nullptr;
     a.k_scale = nullptr;
   }

@@ -222,7 +222,8 @@ class AttnProblem:
     sm_scale: float
     kv_int8: bool = False
     out_fp32: bool = False
-    otf_quant: bool = False   # Q/K INT8 operands made inside the kernel (q_q, q_scale, k_q, k_scale unused)
+    otf_quant: int = 0        # 1 (or True): Q/K INT8 operands made inside the kernel (q_q, q_scale, k_q, k_scale
+                              # unused); 2: Q's alone (q_q, q_scale unused)
     max_seqlen_k: int = 0     # chunked prefill: bound of the key counts (0: prefill)
 
     def params(self) -> AttnParams:
@@ -291,13 +292,14 @@ class AttnPlan:
 
 def tilemix_attn_prefill(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g: int, q_q=None, q_scale=None,
                          k_q=None, k_scale=None, blk_q: int = 64, sm_scale: Optional[float] = None,
-                         kv_int8: bool = False, v_scale=None, out_fp32: bool = False, otf_quant: bool = False,
+                         kv_int8: bool = False, v_scale=None, out_fp32: bool = False, otf_quant: int = 0,
                          cu_seqlens_k=None, max_seqlen_k: int = 0, lse=None, out=None,
                          plan: Optional[AttnPlan] = None, stream=None) -> torch.Tensor:
     """Fused routed causal attention; returns out [N][Hq][d] (fp16, or fp32 if out_fp32).
 
-    otf_quant=False takes the quantise-once operands q_q, q_scale, k_q, k_scale (k_q unused with kv_int8);
-    otf_quant=True makes them inside the kernel and ignores those arguments.  cu_seqlens_k / max_seqlen_k:
+    otf_quant=0 takes the quantise-once operands q_q, q_scale, k_q, k_scale (k_q unused with kv_int8);
+    otf_quant=1 (True) makes them inside the kernel and ignores those arguments; otf_quant=2 makes Q's
+    (q_q, q_scale ignored) and takes k_q, k_scale.  cu_seqlens_k / max_seqlen_k:
     chunked prefill or decode (the queries are the last positions of each sequence's keys).  lse: optional
     float32 [N][Hq] output of each row's log-sum-exp."""
     N, Hq, d = q.shape
@@ -307,7 +309,7 @@ def tilemix_attn_prefill(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g
         sm_scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     if plan is None:
         plan = AttnPlan(AttnProblem(B, int(max_seqlen), Hq, Hk, d, int(g), int(blk_q), float(sm_scale),
-                                    bool(kv_int8), bool(out_fp32), bool(otf_quant), int(max_seqlen_k)),
+                                    bool(kv_int8), bool(out_fp32), int(otf_quant), int(max_seqlen_k)),
                         device=q.device)
     if out is None:
         out = torch.empty((N, Hq, d), dtype=torch.float32 if out_fp32 else torch.float16, device=q.device)
@@ -318,7 +320,7 @@ def tilemix_attn_prefill(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g
 def tilemix_attn_prefill_debug(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g: int, q_q=None,
                                q_scale=None, k_q=None, k_scale=None, blk_q: int = 64,
                                sm_scale: Optional[float] = None, kv_int8: bool = False, v_scale=None,
-                               out_fp32: bool = True, otf_quant: bool = False, cu_seqlens_k=None,
+                               out_fp32: bool = True, otf_quant: int = 0, cu_seqlens_k=None,
                                max_seqlen_k: int = 0, seq: int = 0, q_head: int = 0, m_begin: int = 0,
                                m_end: Optional[int] = None, stream=None):
     """As tilemix_attn_prefill, plus (s32_tiles, visit_count, route_used) debug products."""
@@ -332,7 +334,7 @@ def tilemix_attn_prefill_debug(q, k, v, *, cu_seqlens, route_words, max_seqlen: 
     if sm_scale is None:
         sm_scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     plan = AttnPlan(AttnProblem(B, int(max_seqlen), Hq, Hk, d, int(g), int(blk_q), float(sm_scale), bool(kv_int8),
-                                bool(out_fp32), bool(otf_quant), int(max_seqlen_k)), device=q.device)
+                                bool(out_fp32), int(otf_quant), int(max_seqlen_k)), device=q.device)
     out = torch.empty((N, Hq, d), dtype=torch.float32 if out_fp32 else torch.float16, device=q.device)
     s32 = torch.empty((m_end - m_begin, Tk, TILE, TILE), dtype=torch.int32, device=q.device)
     visits = torch.empty((B, Hq, T, Tk), dtype=torch.int32, device=q.device)

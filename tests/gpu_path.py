@@ -48,6 +48,11 @@ def prepare(w: Workload, dev=DEV, t=None):
 
 def attn(w: Workload, t, out_fp32=True, plan=None, out=None, otf=False, lse=None):
     ck = _chunk_kw(w, t)
+    if otf == 2:   # on-the-fly Q: fp16 q, K quantised once
+        return tm.tilemix_attn_prefill(t["q"], t["k"], t["v"], k_q=t["k_q"], k_scale=t["k_s"], cu_seqlens=t["cu"],
+                                       route_words=t["words"], max_seqlen=w.max_seqlen, g=w.g, blk_q=w.blk_q,
+                                       sm_scale=w.sm_scale, out_fp32=out_fp32, otf_quant=2, plan=plan, out=out,
+                                       lse=lse, **ck)
     if otf:   # on-the-fly quantisation: only fp16 q, k, v, the route words and cu_seqlens
         return tm.tilemix_attn_prefill(t["q"], t["k"], t["v"], cu_seqlens=t["cu"], route_words=t["words"],
                                        max_seqlen=w.max_seqlen, g=w.g, blk_q=w.blk_q, sm_scale=w.sm_scale,
@@ -67,6 +72,9 @@ def attn_debug(w: Workload, t, seq=0, q_head=0, m_begin=0, m_end=None, otf=False
     kw = dict(q_q=t["q_q"], q_scale=t["q_s"], k_scale=t["k_s"], cu_seqlens=t["cu"], route_words=t["words"],
               max_seqlen=w.max_seqlen, g=w.g, blk_q=w.blk_q, sm_scale=w.sm_scale, seq=seq, q_head=q_head,
               m_begin=m_begin, m_end=m_end, **_chunk_kw(w, t))
+    if otf == 2:
+        kw.update(q_q=None, q_scale=None, otf_quant=2)
+        return tm.tilemix_attn_prefill_debug(t["q"], t["k"], t["v"], k_q=t["k_q"], **kw)
     if otf:
         kw.update(q_q=None, q_scale=None, k_scale=None, otf_quant=True)
         return tm.tilemix_attn_prefill_debug(t["q"], t["k"], t["v"], **kw)

@@ -111,8 +111,9 @@ def test_null_pointer_and_workspace_errors(tm):
 
 
 def test_on_the_fly_mode_validation(tm):
-    """otf_quant: 0 or 1, not with an INT8 KV cache; in that mode the quantise-once
-    operands may be NULL (the call then fails only on the missing workspace)."""
+    """otf_quant: 0, 1 or 2, not with an INT8 KV cache.  With 1 the quantise-once
+    operands may be NULL, with 2 those of Q (the call then fails only on the
+    missing workspace); 2 still needs k_q and k_scale."""
     lib = tm.lib()
     a = 1 << 20
     t = tm.AttnTensors(a, a, a, 24 * 128, 128, 8 * 128, 128, None, None, None, None, None, a, a, a)
@@ -122,8 +123,16 @@ def test_on_the_fly_mode_validation(tm):
     p0 = _params(tm).params()
     assert lib.tilemix_attn_prefill(ctypes.byref(p0), ctypes.byref(t), None, 0, None) == 1
     assert "q_q" in tm.last_error()
+    p.otf_quant = 3
+    assert lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 1
     p.otf_quant = 2
     assert lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 1
+    assert "k_scale" in tm.last_error()
+    t.k_q, t.k_scale = a, a
+    assert lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 4
+    with pytest.raises(tm.TilemixError) as e:
+        tm.tilemix_attn_workspace_size(_params(tm, otf_quant=2, kv_int8=True))
+    assert e.value.status == 2
     with pytest.raises(tm.TilemixError) as e:
         tm.tilemix_attn_workspace_size(_params(tm, otf_quant=True, kv_int8=True))
     assert e.value.status == 2 and "kv_int8" in str(e.value)

@@ -288,9 +288,9 @@ OTF_SMALL = [c for c in SMALL if not c[8]]
 @pytest.mark.parametrize("case", OTF_SMALL, ids=[c[0] for c in OTF_SMALL])
 def test_attn_on_the_fly_equals_quantize_once(gp, case):
     """On-the-fly quantisation (Q/K INT8 fragments and block scales made inside
-    the kernel) follows the same blockwise definition as the quantiser, so its
-    output equals the quantise-once output bit for bit (fp32 and fp16 outputs),
-    and therefore meets the oracle bar too."""
+    the kernel, or Q's alone) follows the same blockwise definition as the
+    quantiser, so its output equals the quantise-once output bit for bit (fp32
+    and fp16 outputs), and therefore meets the oracle bar too."""
     import torch
     name, lengths, hq, hk, d, g, route, p, kv8, blk_q, outl = case
     _announce(f"attn on-the-fly {name}")
@@ -302,20 +302,26 @@ def test_attn_on_the_fly_equals_quantize_once(gp, case):
     otf32 = gp.attn(w, t, out_fp32=True, otf=True)
     once16 = gp.attn(w, t, out_fp32=False)
     otf16 = gp.attn(w, t, out_fp32=False, otf=True)
+    qotf32 = gp.attn(w, t, out_fp32=True, otf=2)
+    qotf16 = gp.attn(w, t, out_fp32=False, otf=2)
     torch.cuda.synchronize()
     assert torch.equal(otf32, once32)
     assert torch.equal(otf16, once16)
+    assert torch.equal(qotf32, once32)
+    assert torch.equal(qotf16, once16)
     ma, rf = gp.errors(otf32.cpu().numpy(), orc.attn_prefill(oracle_inputs(w)))
     print(f"  max_abs={ma:.3e} rel_fro={rf:.3e}")
     assert ma <= MAX_ABS and rf <= REL_FRO
 
 
+@pytest.mark.parametrize("mode", [1, 2], ids=["qk", "q"])
 @pytest.mark.parametrize("case", ["tiny", "gqa3_varlen_blkq128"])
-def test_attn_on_the_fly_debug_bitexact(gp, case):
-    """On-the-fly mode: INT32 score tiles bit-exact against the oracle's (so the
-    on-chip Q/K quantisation and block layout are exact), visits and routes too."""
+def test_attn_on_the_fly_debug_bitexact(gp, case, mode):
+    """On-the-fly modes (Q and K, or Q alone): INT32 score tiles bit-exact against
+    the oracle's (so the on-chip quantisation and block layout are exact),
+    visits and routes too."""
     import torch
-    _announce(f"attn on-the-fly debug {case}")
+    _announce(f"attn on-the-fly debug {case} mode {mode}")
     if case == "tiny":
         w = config(1)
         seq, head = 0, 0
@@ -324,7 +330,7 @@ def test_attn_on_the_fly_debug_bitexact(gp, case):
                           p=0.6, outliers=True, blk_q=128)
         seq, head = 1, 4
     t = gp.prepare(w)
-    out, s32, visits, used = gp.attn_debug(w, t, seq=seq, q_head=head, otf=True)
+    out, s32, visits, used = gp.attn_debug(w, t, seq=seq, q_head=head, otf=mode)
     torch.cuda.synchronize()
     inp = oracle_inputs(w)
     assert np.array_equal(s32.cpu().numpy(), orc.s32_tiles(inp, seq, head, 0, w.T))
@@ -794,7 +800,11 @@ def test_standard_config_full_size_sampled(gp, cfg, nsamp):
     w = config(cfg)
     t = gp.prepare(w)
     out = gp.attn(w, t)
+    # the bench's operand mode for an fp16 K/V: Q's INT8 operands made in the kernel
+    qotf = None if w.kv_int8 else gp.attn(w, t, otf=2)
     torch.cuda.synchronize()
+    if qotf is not None:
+        assert torch.equal(qotf, out)
     inp = oracle_inputs(w)
     assert np.array_equal(gp.words_u64(t["words"]), inp.words)
     assert np.array_equal(t["q_q"].cpu().numpy(), inp.q_q)
