@@ -23,7 +23,9 @@
 // plan: one workgroup.  Tile counts and the rank sort live in LDS (global
 //   scratch past kPlanLdsBatch sequences); the greedy placement runs in wave 0
 //   with one XCD per lane and writes each segment to the segment table without
-//   reading it back, then the segment count and per-XCD fill levels.
+//   reading it back, then the segment count and per-XCD fill levels.  A
+//   sequence's KV-head groups are identical jobs; up to eight of them are
+//   placed in one step where that gives the same result as one at a time.
 // emit: one workgroup per segment writes that segment's items; 8 more
 //   workgroups mark each XCD's unused slots empty (b = -1).
 #include "device_common.hpp"
@@ -92,7 +94,42 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
       tiles_b += (uint64_t)tb * (uint32_t)max(lead, 0) / kTile;
     }
     const uint32_t cost = (uint32_t)(((uint64_t)a.nch * tiles_b) >> a.cost_shift);
-    for (int hk = 0; hk < a.Hk; ++hk) {
+    for (int hk = 0; hk < a.Hk;) {
+      // The sequence's Hk groups are identical jobs.  When every XCD has room
+      // for a whole group and one group's cost moves the least-loaded XCD's key
+      // past the k-th smallest key, placing k groups one by one gives group
+      // hk + i to the XCD of rank i: all k are placed at once.
+      {
+        const int k = min(a.Hk - hk, kNumXcd);
+        const uint32_t key = lane < kNumXcd ? (load << 3) | (uint32_t)lane : 0xFFFFFFFFu;
+        uint32_t rank = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int y = 0; y < kNumXcd; ++y) {
+          const uint32_t ky = (uint32_t)__builtin_amdgcn_readlane((int)key, y);
+          rank += ky < key;
+          kmin = min(kmin, ky);
+        }
+        const bool room = lane >= kNumXcd || cap - used >= cnt;
+        const uint64_t kth = __ballot(lane < kNumXcd && rank == (uint32_t)(k - 1));
+        const uint32_t keyk = (uint32_t)__builtin_amdgcn_readlane((int)key, (int)__builtin_ctzll(kth));
+        if (k > 1 && __all(room) && (uint64_t)kmin + ((uint64_t)cost << 3) > keyk &&
+            nseg + (uint32_t)k <= segmax) {
+          if (lane < kNumXcd && rank < (uint32_t)k) {
+            int32_t* sg = a.seg + (int64_t)(nseg + rank) * kSegFields;
+            sg[0] = lane;
+            sg[1] = (int32_t)used;
+            sg[2] = (int32_t)cnt;
+            sg[3] = 0;
+            sg[4] = b;
+            sg[5] = hk + (int)rank;
+            used += cnt;
+            load += cost;
+          }
+          nseg += (uint32_t)k;
+          hk += k;
+          continue;
+        }
+      }
       uint32_t remaining = cnt, ib = 0;
       while (remaining > 0 && nseg < segmax) {
         const bool fits = lane < kNumXcd && cap - used >= remaining;
@@ -128,6 +165,7 @@ __global__ __launch_bounds__(256) void schedule_plan_kernel(SchedArgs a) {
         ib += take;
         remaining -= take;
       }
+      ++hk;
     }
   }
   if (lane == 0) a.segidx[0] = (int32_t)nseg;

@@ -421,6 +421,89 @@ def test_attn_int8_score_scale_extremes(gp, case):
         assert ma <= MAX_ABS and rf <= REL_FRO
 
 
+def _greedy_plan(cu, T, Hk, nch, cu_k=None):
+    """Work list of the XCD planner, placing one (sequence, KV head) group at a
+    time: groups in decreasing tile count, each whole on the XCD with the least
+    load (lowest index on ties) that has room, else split over the XCDs with
+    the most free slots; slot i takes entry i // 8 of XCD i % 8's list."""
+    xcd = 8
+    lens = np.diff(cu).astype(np.int64)
+    tiles = (lens + 63) // 64
+    B = len(lens)
+    items_n = B * T * Hk * nch
+    nslots = max(-(-items_n // xcd) * xcd, xcd)
+    cap = nslots // xcd
+    Tk = T if cu_k is None else int(-(-int(np.diff(cu_k).max()) // 64))
+    rows = B * Hk * nch * T
+    total = rows * (T + 1) // 2 + (rows * Tk if cu_k is not None else 0)
+    shift = 0
+    while (total >> shift) >= (1 << 28):
+        shift += 1
+    order = sorted(range(B), key=lambda b: (-tiles[b], b))
+    used, load = [0] * xcd, [0] * xcd
+    items = np.zeros((nslots, 4), np.int32)
+    items[:, 0] = -1
+    for b in order:
+        tb = int(tiles[b])
+        if tb == 0:
+            break
+        cnt = tb * nch
+        tb_cost = tb * (tb + 1) // 2
+        if cu_k is not None:
+            lead = int(cu_k[b + 1] - cu_k[b]) - int(lens[b])
+            tb_cost += tb * max(lead, 0) // 64
+        cost = (nch * tb_cost) >> shift
+        for hk in range(Hk):
+            remaining, ib = cnt, 0
+            while remaining > 0:
+                fits = [x for x in range(xcd) if cap - used[x] >= remaining]
+                if fits:
+                    best = min(fits, key=lambda x: (load[x], x))
+                    take = remaining
+                else:
+                    best = max(range(xcd), key=lambda x: (cap - used[x], -x))
+                    take = cap - used[best]
+                for i in range(take):
+                    t = ib + i
+                    items[(used[best] + i) * xcd + best] = (b, hk, tb - 1 - t // nch, t % nch)
+                load[best] += cost if take == cnt else cost * take // cnt
+                used[best] += take
+                ib += take
+                remaining -= take
+    return items
+
+
+@pytest.mark.parametrize("case", ["equal_B8_hk8", "varlen_hk16", "varlen_hk5_chunks", "many_short"])
+def test_plan_matches_greedy_placement(gp, case):
+    """The work list equals the one-group-at-a-time greedy placement (the plan
+    kernel places a sequence's identical KV-head groups in one step where that
+    gives the same result)."""
+    import torch
+    _announce(f"plan vs greedy {case}")
+    rng = np.random.default_rng(5)
+    if case == "equal_B8_hk8":
+        lens, hq, hk = [4096] * 8, 24, 8
+    elif case == "varlen_hk16":
+        lens, hq, hk = [int(x) for x in rng.integers(1, 3000, 11)], 32, 16
+    elif case == "varlen_hk5_chunks":
+        lens, hq, hk = [int(x) for x in rng.integers(1, 2000, 9)], 35, 5
+    else:
+        lens, hq, hk = [int(x) for x in rng.integers(1, 200, 300)], 8, 8
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    L = max(lens)
+    prob = gp.tm.AttnProblem(len(lens), L, hq, hk, 128, 1, 64, 0.088, False, True)
+    plan = gp.tm.AttnPlan(prob, "cuda:0")
+    plan.schedule(torch.from_numpy(cu).to("cuda:0"))
+    torch.cuda.synchronize()
+    T = -(-L // 64)
+    nch = -(-(hq // hk) // 3)
+    ref = _greedy_plan(cu, T, hk, nch)
+    got = plan.workspace[:ref.size * 4].cpu().view(torch.int32).numpy().reshape(-1, 4)
+    live = ref[:, 0] >= 0
+    assert np.array_equal(got[live], ref[live])
+    assert np.all(got[~live, 0] == -1)
+
+
 def test_attn_plan_then_run_equals_prefill(gp):
     """tilemix_attn_plan + tilemix_attn_run give the same bits as tilemix_attn_prefill,
     and one plan serves repeated runs."""
