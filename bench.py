@@ -413,20 +413,16 @@ def main():
     work = work_model(w, words.cpu().numpy().view(np.uint64))
 
     # The route words and the work list depend only on the routing template and
-    # cu_seqlens: the work list is built on a second stream (default priority)
-    # beside the quantiser, and the attention waits for both.  The route words go
-    # with the shorter branch: beside the quantiser when it covers Q (or V) too,
-    # after it when it covers K alone.  (Quantising K on a third stream beside Q
-    # measured no faster: both are HBM-bound, and each cross-stream wait costs
-    # several microseconds.)
+    # cu_seqlens: they are built on a second stream (default priority) beside the
+    # quantiser, and the attention waits for both.  (Quantising K on a third
+    # stream beside Q measured no faster: both are HBM-bound, and each
+    # cross-stream wait costs several microseconds.)
     side = torch.cuda.Stream(device=dev)
-    route_on_side = mode == 0 or w.kv_int8
 
     def step(ev=None, stream=stream):
         side.wait_stream(stream)                 # the previous step's attention has read words / work list
         with torch.cuda.stream(side):
-            if route_on_side:
-                tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=side)
+            tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=side)
             plan.schedule(cu, stream=side)
         if mode == 0:
             tm.tilemix_quantize_blockwise(q, cu, w.max_seqlen, w.blk_q, q_q, q_s, stream=stream)
@@ -434,8 +430,6 @@ def main():
             tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
         if w.kv_int8:
             tm.tilemix_quantize_blockwise(v, cu, w.max_seqlen, 64, v_q, v_s, stream=stream)
-        if not route_on_side:
-            tm.tilemix_build_route_mask(tr, cu, w.max_seqlen, w.g, words, stream=stream)
         stream.wait_stream(side)
         if ev is not None:
             ev[0].record(stream)
