@@ -661,6 +661,7 @@ def test_attn_chunked_full(gp, case):
     lse = torch.empty((w.q.shape[0], hq), dtype=torch.float32, device="cuda:0")
     out = gp.attn(w, t, lse=lse)
     otf = None if kv8 else gp.attn(w, t, otf=True)
+    qotf = None if kv8 else gp.attn(w, t, otf=2)
     torch.cuda.synchronize()
     ref, ref_lse = orc.attn_prefill(oracle_inputs(w), with_lse=True)
     ma, rf = gp.errors(out.cpu().numpy(), ref)
@@ -668,11 +669,13 @@ def test_attn_chunked_full(gp, case):
     print(f"  max_abs={ma:.3e} rel_fro={rf:.3e} lse_err={le:.3e}")
     assert ma <= MAX_ABS and rf <= REL_FRO
     assert le <= LSE_ABS
-    if otf is not None:
+    for o in (otf, qotf):   # operands made in the kernel (Q and K, or Q alone)
+        if o is None:
+            continue
         if max(Lq) > 1:
-            assert torch.equal(otf, out)
+            assert torch.equal(o, out)
         else:   # decode goes to the decode kernel, on-the-fly to the prefill kernel: other order
-            mo, ro = gp.errors(otf.cpu().numpy(), ref)
+            mo, ro = gp.errors(o.cpu().numpy(), ref)
             assert mo <= MAX_ABS and ro <= REL_FRO
 
 
