@@ -664,8 +664,11 @@ void attn_prefill_kernel(const AttnArgs a) {
   }
 
   // on-the-fly Q: Q block scales and the INT8 Q operands (channels
-  // 64 ds + 16 gq .. +15 of the lane's query row)
+  // 64 ds + 16 gq .. +15 of the lane's query row).  The waves raise their
+  // priority for this block, so the other workgroup on the CU yields the issue
+  // port until the item can start its tiles (measured ~0.4 % faster).
   if (QOTF) {
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       float sq = 1.0f;
@@ -689,6 +692,7 @@ void attn_prefill_kernel(const AttnArgs a) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Tile n: tile n+1's loads are issued first (into the other stage, last
