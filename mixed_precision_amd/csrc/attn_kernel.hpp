@@ -801,12 +801,16 @@ void attn_prefill_kernel(const AttnArgs a) {
     if (OTF && rnext && !last) A::k_partial_amax(next, wave, lane);
     __syncthreads();
     // LDS staging: every wave is done with the stage and the raw next tile
-    // has landed; widen it into the stage (skipped after the last tile)
+    // has landed; widen it into the stage (skipped after the last tile), at
+    // raised priority: the workgroup cannot start the tile before it is done,
+    // and the other workgroup on the CU yields meanwhile (~1 % faster)
     if (RAWST && !last) {
       const typename A::VSplit vn = A::vsplit(vscale_row[n + 1]);
       typename A::Stage st;
+      __builtin_amdgcn_s_setprio(2);
       A::stage_from_lds(st, tid, raw);
       A::stage_store(st, rnext, tid, next, next + A::KBYTES, vn.s2, vn.b2);
+      __builtin_amdgcn_s_setprio(0);
       lds_barrier();
     }
     // next tile's group, in integer arithmetic (left >= 1; a compare here
