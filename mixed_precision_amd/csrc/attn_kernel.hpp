@@ -717,8 +717,10 @@ void attn_prefill_kernel(const AttnArgs a) {
     if (OTF) {
       ksc = 1.0f;
       if (rc) {
+        __builtin_amdgcn_s_setprio(2);   // (the tile waits for it: the other workgroup yields)
         ksc = uniform(A::k_tile_scale(cur));
         A::quant_k(cur, k8s, ksc, wave, lane);
+        __builtin_amdgcn_s_setprio(0);
         lds_barrier();
       }
     } else {
