@@ -760,8 +760,9 @@ void attn_prefill_kernel(const AttnArgs a) {
     for (int h = 0; h < 2; ++h) {
       i32x4 S[QB][2];
       // a wave issuing MFMAs gets priority, so the other wave of the SIMD runs
-      // its softmax in their shadow
-      __builtin_amdgcn_s_setprio(1);
+      // its softmax in their shadow; QK^T, which starts the half's dependent
+      // chain, ranks above P.V
+      __builtin_amdgcn_s_setprio(2);
       if (rc == 0) {
         A::qk16(kl, h, qf, S, c, gq);
       } else {
