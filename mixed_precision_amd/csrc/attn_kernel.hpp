@@ -761,7 +761,7 @@ void attn_prefill_kernel(const AttnArgs a) {
       i32x4 S[QB][2];
       // a wave issuing MFMAs gets priority, so the other wave of the SIMD runs
       // its softmax in their shadow; QK^T, which starts the half's dependent
-      // chain, ranks above P.V
+      // chain, ranks highest
       __builtin_amdgcn_s_setprio(2);
       if (rc == 0) {
         A::qk16(kl, h, qf, S, c, gq);
@@ -789,7 +789,9 @@ void attn_prefill_kernel(const AttnArgs a) {
       __builtin_amdgcn_s_setprio(0);
       f16x8 P[QB];
       A::softmax(S, cj, lmv, nref, lrow, lacc, O, P);
-      __builtin_amdgcn_s_setprio(1);
+      // P.V: above the softmax with up to two heads per item; with three it
+      // stays at 0, so only QK^T preempts (measured both ways per head count)
+      __builtin_amdgcn_s_setprio(QB == 3 ? 0 : 1);
       A::pv(vl, h, P, O, lacc, lrow, rmv, lane);
       __builtin_amdgcn_s_setprio(0);
     }
