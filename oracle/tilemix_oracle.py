@@ -565,17 +565,20 @@ def attn_dense_two_pass(inp: AttnInputs, b: int, hq: int, with_lse: bool = False
     return P @ vf
 
 
-def attn_brute_force(inp: AttnInputs, b: int, hq: int) -> List[List[float]]:
+def attn_brute_force(inp: AttnInputs, b: int, hq: int, with_lse: bool = False):
     """Element-by-element evaluation in plain Python for tiny L: each score from
     its own definition (route bit decoded per element, INT8 dot product summed
-    as Python integers), then softmax of each row and the weighted sum of values."""
+    as Python integers; with an INT8 KV cache each key and value element is
+    dequantised with the scale of its own 64-key block, looked up per element),
+    then softmax of each row and the weighted sum of values.  Returns the rows
+    ([Lq][d] lists); with_lse: also each row's log-sum-exp of its scores."""
     s0, _ = inp.spans[b]
     k0, _ = inp.spans_k[b]
     Lq, Lk = inp.pairs[b]
     d = inp.d
     hk = inp.kv_head(hq)
     sm = inp.sm
-    out = []
+    out, lses = [], []
     for i in range(Lq):
         word = int(inp.words[hk, b, i // BLOCK_M])
         scores = []
@@ -595,6 +598,7 @@ def attn_brute_force(inp: AttnInputs, b: int, hq: int) -> List[List[float]]:
         mx = max(scores)
         e = [math.exp(s - mx) for s in scores]
         z = sum(e)
+        lses.append(mx + math.log(z))
         row = []
         for c in range(d):
             acc = 0.0
@@ -606,7 +610,7 @@ def attn_brute_force(inp: AttnInputs, b: int, hq: int) -> List[List[float]]:
                 acc += e[j] * vv
             row.append(acc / z)
         out.append(row)
-    return out
+    return (out, lses) if with_lse else out
 
 
 # ---------------------------------------------------------------------------

@@ -199,6 +199,66 @@ def test_pin_G_kv_int8_row0_is_dequantised_v():
     assert np.array_equal(out[0, 0], ref)
 
 
+# ---------------------------------------------------------------- pin E, INT8 KV cache
+def _kv_blocks_scaled(w, rng):
+    """Scale K and V of every (sequence, 64-key block, KV head) by its own factor
+    e^u, u ~ U(-4, 4), before quantisation, so the per-block scales of one
+    sequence spread over more than three orders of magnitude: a scale looked up
+    in the wrong block then moves the result far outside the tolerance."""
+    cu_k = w.cu_seqlens if w.cu_seqlens_k is None else w.cu_seqlens_k
+    for s0, L in orc.seq_spans(cu_k):
+        for b0 in range(0, L, 64):
+            r0, r1 = s0 + b0, s0 + min(b0 + 64, L)
+            for arr in (w.k, w.v):
+                f = np.exp(rng.uniform(-4.0, 4.0, size=(1, arr.shape[1], 1)))
+                arr[r0:r1] = (arr[r0:r1].astype(np.float64) * f).astype(np.float16)
+
+
+def _check_kv_int8_brute_force(w, inp):
+    out, lse = orc.attn_prefill(inp, with_lse=True)
+    routes = set()
+    for b, (s0, Lq) in enumerate(orc.seq_spans(w.cu_seqlens)):
+        for hq in range(w.num_q_heads):
+            bf, bl = orc.attn_brute_force(inp, b, hq, with_lse=True)
+            bf, bl = np.array(bf), np.array(bl)
+            tol = 1e-12 * max(1.0, float(np.max(np.abs(bf))))
+            assert np.max(np.abs(out[s0:s0 + Lq, hq] - bf)) <= tol
+            assert np.max(np.abs(lse[s0:s0 + Lq, hq] - bl)) <= 1e-12 * max(1.0, float(np.max(np.abs(bl))))
+            hk = inp.kv_head(hq)
+            for m in range(orc.num_tiles(Lq)):
+                for n in range(orc.last_key_tile(m, *inp.pairs[b]) + 1):
+                    routes.add(orc.route_bit(int(inp.words[hk, b, m]), n, w.g))
+    assert routes == {0, 1}                       # both score paths were exercised
+
+
+@pytest.mark.parametrize("g", [1, 2])
+def test_pin_E_brute_force_kv_int8(g):
+    """INT8 KV cache (K_eff = k8 s_k, V_eff = v8 s_v, one scale per 64-key block,
+    [PL App. C]): the streaming oracle's rows and log-sum-exp against the
+    element-by-element brute force, which dequantises every key and value
+    element with the scale of its own block.  Two sequences of 3 and 2 key
+    blocks (the last ones partial), GQA 2:1 over two KV heads, both routes,
+    block scales spread over e^+-4 per block and head."""
+    w = _small([150, 70], hq=4, hk=2, d=64, g=g, p=0.5, cfg=232 + g, outliers=True, kv_int8=True)
+    _kv_blocks_scaled(w, np.random.default_rng(33 + g))
+    inp = oracle_inputs(w)
+    for sc in (inp.k_scale, inp.v_scale):       # the spread the pin relies on
+        assert sc[:, 0, :3].max() / sc[:, 0, :3].min() > 20
+    _check_kv_int8_brute_force(w, inp)
+
+
+def test_pin_M_chunked_brute_force_kv_int8():
+    """Chunked prefill and decode over an INT8 KV cache against the brute force:
+    queries are the last Lq of Lk keys, so their keys span every block of the
+    cache (block scales spread as above)."""
+    w = make_chunked_workload(292, lengths_q=[70, 1, 5], lengths_k=[200, 130, 5], num_q_heads=4, num_kv_heads=2,
+                              head_dim=64, g=1, p=0.5, outliers=True, kv_int8=True)
+    _kv_blocks_scaled(w, np.random.default_rng(34))
+    inp = oracle_inputs(w)
+    assert inp.k_scale[:, 0, :4].max() / inp.k_scale[:, 0, :4].min() > 20
+    _check_kv_int8_brute_force(w, inp)
+
+
 # ---------------------------------------------------------------- pin H
 def test_pin_H_quantizer_invariants_and_exact_rounding():
     rng = np.random.default_rng(11)
