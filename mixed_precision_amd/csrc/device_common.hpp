@@ -96,9 +96,10 @@ TM_DEV uint32_t wave_max_u32(uint32_t v) {
 //  * scale and r = fl32(1/scale) are correctly rounded divisions, once per
 //    block; per element q0 = fl32(x r), e = x - q0 scale (one fma, exact) and
 //    q1 = fl32(q0 + e r) is the correctly rounded quotient fl32(x/scale) (the
-//    correction step of Markstein's division; checked for every finite fp16 x
-//    with |x| <= a against every scale a fp16 block can produce: the only
-//    difference is the sign of a zero quotient, which does not reach the int8);
+//    correction step of Markstein's division).  tests/quant_division_exhaustive.c
+//    replays these steps for every finite fp16 x with |x| <= a against every
+//    scale a fp16 block can produce: the only difference is the sign of a zero
+//    quotient, which does not reach the int8;
 //  * adding 1.5 * 2^23 rounds q1 to an integer with ties to even, and the low
 //    byte of the sum's bit pattern is that integer in two's complement;
 //  * |q1| <= 127 (1 + 2^-23) because scale >= a/127 (1 - 2^-24), so the clamp
