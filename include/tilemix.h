@@ -202,14 +202,20 @@ typedef struct {
   const void* k;          /* kv_int8 = 0: fp16; 1: int8.  k[t*kv_stride_tok + h*kv_stride_head + c] */
   const void* v;          /* same type and strides as k */
   int64_t q_stride_tok, q_stride_head;    /* elements; multiples of 8; 16-byte aligned base */
-  int64_t kv_stride_tok, kv_stride_head;  /* elements; multiples of 8 (fp16) or 16 (int8) */
+  int64_t kv_stride_tok, kv_stride_head;  /* elements; multiples of 8 (fp16) or 16 (int8); 64 rows at
+                                             the token stride must span less than 4 GiB (a tile is read
+                                             through one 32-bit buffer range), else
+                                             TILEMIX_ERR_UNSUPPORTED */
   const int8_t* q_q;      /* int8 [N][Hq][d] contiguous, from tilemix_quantize_blockwise(q, blk_q);
                              unused when otf_quant = 1 or 2 */
   const float* q_scale;   /* float32 [Hq][batch][ceil(max_seqlen/blk_q)]; unused when otf_quant = 1 or 2 */
   const int8_t* k_q;      /* kv_int8 = 0: int8 [N][Hk][d] contiguous (quantize_blockwise(k, 64));
                              unused when kv_int8 = 1 or otf_quant = 1 */
   const float* k_scale;   /* float32 [Hk][batch][Tk]: per 64-token block of K; unused when otf_quant = 1 */
-  const float* v_scale;   /* kv_int8 = 1: float32 [Hk][batch][Tk]; 0: unused */
+  const float* v_scale;   /* kv_int8 = 1: float32 [Hk][batch][Tk]; 0: unused.  Supported values: 0 (an
+                             all-zero block) and [2^-31, 65504/127], the range the quantiser makes from
+                             fp16 data; larger values can overflow the fp16 probabilities, smaller ones
+                             lose precision in the row sum.  Not checked (device data). */
   const int32_t* cu_seqlens;     /* int32 [batch+1]: queries (and keys, in prefill) */
   const uint64_t* route_words;   /* uint64 [Hk][batch][T] from tilemix_build_route_mask */
   void* out;              /* fp16 or float32 [N][Hq][d] contiguous (written) */

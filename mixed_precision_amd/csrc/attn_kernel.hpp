@@ -252,11 +252,18 @@ struct Attn {
       r.v[i] = *reinterpret_cast<const u32x4*>(raw + 64 * D + 16 * (tid + 256 * i));
     }
   }
-  // INT8 V: the tile's scale s_v = mv 2^E with E = min(exponent, 5) >= -24 and
-  // mv in [1, 16) (scales below 2^-24 take E = -24, mv = 1).  V is widened
-  // exactly to v8 2^E, the mantissa mv goes into P (log2 mv added in the
-  // exponent) and the row sum adds P / mv: the P.V numerator and the row sum
-  // then use the same rounded weights, as with fp16 V.
+  // INT8 V: the tile's scale s_v = mv 2^E.  V is widened exactly to v8 2^E,
+  // the mantissa mv goes into P (log2 mv added in the exponent) and the row
+  // sum adds P / mv: the P.V numerator and the row sum then use the same
+  // rounded weights, as with fp16 V.
+  //  * s_v >= 2^-24: E = min(exponent, 5) and mv in [1, 16.2) for every scale
+  //    up to 65504/127, the largest the quantiser makes from fp16 data (larger
+  //    scales would let P overflow fp16 and are outside the supported range);
+  //  * 0 < s_v < 2^-24: E = -24 (v8 2^-24 is still exact in fp16) and
+  //    mv = s_v 2^24 < 1 (at least 2^-7 for any scale the quantiser makes:
+  //    fp16 data give s_v >= 2^-24 / 127);
+  //  * s_v = 0 (an all-zero block, as a caller may store it): V widens to zeros
+  //    and mv = 1, so the block's probabilities still count in the row sum.
   struct VSplit {
     float lmv, rmv;   // log2 mv, 1 / mv
     f16x2 s2, b2;     // 2^E and -1152 2^E for the widening fma
@@ -264,11 +271,13 @@ struct Attn {
   static TM_DEV VSplit vsplit(float vsc) {
     int E = -24;
     float mv = 1.0f;
-    if (vsc >= 0x1p-24f && vsc <= 65504.0f) {
+    if (vsc >= 0x1p-24f) {
       E = min((int)((__builtin_bit_cast(uint32_t, vsc) >> 23) & 0xFF) - 127, 5);
       mv = __builtin_ldexpf(vsc, -E);
+    } else if (vsc > 0.0f) {
+      mv = vsc * 0x1p24f;   // exact
     }
-    const float p2 = __builtin_ldexpf(1.0f, E);
+    const float p2 = vsc > 0.0f ? __builtin_ldexpf(1.0f, E) : 0.0f;
     VSplit v;
     v.lmv = __builtin_amdgcn_logf(mv);
     v.rmv = 1.0f / mv;
@@ -584,8 +593,9 @@ void attn_prefill_kernel(const AttnArgs a) {
   }
 
   // ---- sources: this sequence's key rows of KV head hk.  Per tile the buffer
-  // base moves to the tile's first row and the range shrinks to the rows left,
-  // so rows >= Lk read as zero.
+  // base moves to the tile's first row and the range covers the tile's own
+  // rows (at most 64, fewer at the sequence end), so rows >= Lk read as zero
+  // and the 32-bit range cannot wrap (the host keeps 64 rows below 4 GiB).
   const int64_t esz = KVI8 ? 1 : 2;
   const char* kbase = static_cast<const char*>(a.k) + ((int64_t)kseq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
   const char* vbase = static_cast<const char*>(a.v) + ((int64_t)kseq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
@@ -595,7 +605,7 @@ void attn_prefill_kernel(const AttnArgs a) {
       (KVI8 || OTF) ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)kseq0 * a.Hk + hk) * D);
   // (empty: a zero-length range, the load reads zeros and touches no memory)
   auto tile_rsrc = [&](const char* base, uint32_t stride, int n, bool empty) __attribute__((always_inline)) {
-    const int rows = empty ? 0 : max(Lk - n * kTile, 0);
+    const int rows = empty ? 0 : min(max(Lk - n * kTile, 0), kTile);
     return make_rsrc(base + (int64_t)n * kTile * stride, (uint32_t)rows * stride);
   };
   typename A::Dma dma;

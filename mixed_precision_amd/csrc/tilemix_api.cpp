@@ -152,6 +152,12 @@ int32_t validate_tensors(const tilemix_attn_params* p, const tilemix_attn_tensor
     return fail(TILEMIX_ERR_INVALID_ARG, "k/v strides must be positive multiples of %lld elements", (long long)kv_mult);
   if (t->q_stride_head < p->head_dim && t->q_stride_tok < p->head_dim)
     return fail(TILEMIX_ERR_INVALID_ARG, "q strides overlap the channel dimension");
+  // a K/V tile (64 rows at the token stride) is read through one buffer
+  // descriptor whose byte range is 32-bit
+  const int64_t tile_span = t->kv_stride_tok * (p->kv_int8 ? 1 : 2) * kTile;
+  if (tile_span >= ((int64_t)1 << 32))
+    return fail(TILEMIX_ERR_UNSUPPORTED, "k/v token stride of %lld elements: 64 rows span %lld bytes, 4 GiB or more",
+                (long long)t->kv_stride_tok, (long long)tile_span);
   return TILEMIX_OK;
 }
 

@@ -5,6 +5,8 @@ Every operand the attention call consumes is produced by the library itself
 arrays, so the two share only the seeded inputs."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -87,7 +89,19 @@ def words_u64(words: torch.Tensor) -> np.ndarray:
     return words.cpu().numpy().view(np.uint64)
 
 
-def errors(got: np.ndarray, ref: np.ndarray):
+# (test id, max-abs error, relative Frobenius error) of every comparison made
+# through errors(); the session prints them as a margin table at the end
+MARGINS = []
+
+
+def record(ma: float, rf: float, label: str = "") -> None:
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0].split("::")[-1]
+    MARGINS.append((test + (f" [{label}]" if label else ""), ma, rf))
+
+
+def errors(got: np.ndarray, ref: np.ndarray, label: str = ""):
     got = got.astype(np.float64)
     diff = got - ref
-    return float(np.max(np.abs(diff))), float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+    ma, rf = float(np.max(np.abs(diff))), float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+    record(ma, rf, label)
+    return ma, rf

@@ -197,3 +197,21 @@ def test_quantize_and_route_validation(tm):
     assert lib.tilemix_build_route_mask(a, a, a, 1, 64, 0, 1, 1, a, None) == 1
     assert lib.tilemix_build_route_mask(a, a, None, 1, 64, 128, 1, 1, a, None) == 1
     assert lib.tilemix_build_route_mask(a, a, a, 1, 128, 64, 1, 1, a, None) == 1
+
+
+def test_kv_stride_tile_span_limit(tm):
+    """A K/V tile is read through one 32-bit buffer range: a token stride whose
+    64 rows span 4 GiB or more is rejected on the host (fp16: stride >= 2^25
+    elements; INT8 cache: >= 2^26), one element of stride less is accepted (the
+    call then fails only on the missing workspace)."""
+    lib = tm.lib()
+    a = 1 << 20
+    p16 = _params(tm).params()
+    p8 = _params(tm, kv_int8=True).params()
+    for p, limit in ((p16, 1 << 25), (p8, 1 << 26)):
+        t = tm.AttnTensors(a, a, a, 24 * 128, 128, limit, 128, a, a, a, a, a, a, a, a)
+        assert lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 2
+        assert "4 GiB" in tm.last_error()
+        assert lib.tilemix_attn_run(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 2
+        t.kv_stride_tok = limit - 16
+        assert lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 4

@@ -854,60 +854,138 @@ def test_attn_prefill_lse(gp):
     assert float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse))) <= LSE_ABS
 
 
-def _samples(w, rng, n):
+def _sample_rows(w, rng, n):
+    """(sequence, query-tile row) samples of a full-size workload: tiles 0, 1,
+    T-1 and T-2 of the longest, the shortest and the first sequence, the first
+    and last tile of route groups (g boundaries), then random rows up to n."""
     spans = orc.seq_spans(w.cu_seqlens)
     lens = [L for _, L in spans]
     out = set()
-    G = w.num_q_heads // w.num_kv_heads
     b_long, b_short = int(np.argmax(lens)), int(np.argmin(lens))
-    for b in {b_long, b_short, 0}:
+    for b in sorted({b_long, b_short, 0}):
         Tb = orc.num_tiles(lens[b])
-        for m in {0, 1, Tb - 1, Tb - 2}:
+        for m in (0, 1, Tb - 1, Tb - 2):
             if 0 <= m < Tb:
-                for hk in range(w.num_kv_heads):
-                    out.add((b, hk * G + int(rng.integers(G)), m))
-        for j in range(0, min(64, (Tb + w.g - 1) // w.g)):   # group boundaries
-            for m in (j * w.g, j * w.g + w.g - 1):
+                out.add((b, m))
+        for j in range(1, min(64, (Tb + w.g - 1) // w.g)):   # group boundaries
+            for m in (j * w.g - 1, j * w.g):
                 if m < Tb and len(out) < n // 2:
-                    out.add((b, int(rng.integers(w.num_q_heads)), m))
+                    out.add((b, m))
     while len(out) < n:
         b = int(rng.integers(len(lens)))
-        out.add((b, int(rng.integers(w.num_q_heads)), int(rng.integers(orc.num_tiles(lens[b])))))
+        out.add((b, int(rng.integers(orc.num_tiles(lens[b])))))
     return sorted(out)
 
 
-@pytest.mark.parametrize("cfg,nsamp", [(2, 96), (3, 48), (4, 24), (5, 12)])
-def test_standard_config_full_size_sampled(gp, cfg, nsamp):
-    """Full-size workloads in the launch configuration the bench times, checked
-    on sampled query-tile rows (the oracle evaluates each one by one), plus
-    the full int8 operands and route words bit-exact."""
+def _nan_out(w, dev="cuda:0"):
     import torch
-    _announce(f"config {cfg} full size sampled ({nsamp} rows)")
-    w = config(cfg)
-    t = gp.prepare(w)
-    out = gp.attn(w, t)
-    # the bench's operand mode for an fp16 K/V: Q's INT8 operands made in the kernel
-    qotf = None if w.kv_int8 else gp.attn(w, t, otf=2)
-    torch.cuda.synchronize()
-    if qotf is not None:
-        assert torch.equal(qotf, out)
-    inp = oracle_inputs(w)
-    assert np.array_equal(gp.words_u64(t["words"]), inp.words)
-    assert np.array_equal(t["q_q"].cpu().numpy(), inp.q_q)
-    assert np.array_equal(t["q_s"].cpu().numpy(), inp.q_scale)
-    rng = np.random.default_rng(cfg)
-    got_all = out.cpu().numpy()
-    errs, num, den = [], 0.0, 0.0
-    for (b, hq, m) in _samples(w, rng, nsamp):
+    return torch.full((int(w.cu_seqlens[-1]), w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32,
+                      device=dev)
+
+
+def _compare_rows(gp, inp, got_all, rows, label=""):
+    """Max-abs and relative Frobenius error of the sampled tile rows {(b, hq, m): ref}."""
+    num = den = 0.0
+    ma = 0.0
+    for (b, hq, m), ref in rows.items():
         s0, L = inp.spans[b]
-        i0, i1 = m * 64, min(m * 64 + 64, L)
-        ref = orc.attn_tile_row(inp, b, hq, m)
-        got = got_all[s0 + i0:s0 + i1, hq].astype(np.float64)
-        errs.append(np.max(np.abs(got - ref)))
+        got = got_all[s0 + m * 64:s0 + min(m * 64 + 64, L), hq].astype(np.float64)
+        ma = max(ma, float(np.max(np.abs(got - ref))))
         num += float(np.sum((got - ref) ** 2))
         den += float(np.sum(ref ** 2))
-    ma, rf = max(errs), (num / den) ** 0.5
-    print(f"  {w.name}: max_abs={ma:.3e} rel_fro={rf:.3e} over {len(errs)} tile rows")
+    rf = (num / den) ** 0.5
+    gp.record(ma, rf, label)
+    return ma, rf
+
+
+def _operands_bitexact(gp, w, t, inp):
+    """Route words, Q8 and its scales, and K8 / K scales (INT8 cache: K8, V8 and
+    both scales) of the library equal the oracle's, in full."""
+    assert np.array_equal(gp.words_u64(t["words"]), inp.words)
+    assert np.array_equal(t["q_q"].cpu().numpy(), inp.q_q)
+    assert np.array_equal(t["q_s"].cpu().numpy().view(np.uint32), inp.q_scale.view(np.uint32))
+    kq = t["k8"] if w.kv_int8 else t["k_q"]
+    assert np.array_equal(kq.cpu().numpy(), inp.k_q)
+    assert np.array_equal(t["k_s"].cpu().numpy().view(np.uint32), inp.k_scale.view(np.uint32))
+    if w.kv_int8:
+        assert np.array_equal(t["v8"].cpu().numpy(), inp.v_q)
+        assert np.array_equal(t["v_s"].cpu().numpy().view(np.uint32), inp.v_scale.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg,nsamp", [(2, 0), (3, 16), (4, 12), (5, 12)])
+def test_standard_config_full_size(gp, cfg, nsamp):
+    """Full-size workloads in the launch configuration the bench times.  The
+    output buffers start as NaN and every element must come back finite (a
+    work item dropped or never written would show).  All INT8 operands, their
+    scales and the route words are bit-exact in full.  The 3B-shaped layer
+    (config 2) is compared with the oracle in full, every row of every head;
+    configs 3-5 on sampled query-tile rows, every query head of each.  For an
+    fp16 K/V the bench's operand mode (Q's INT8 operands made in the kernel)
+    gives the same bits."""
+    import torch
+    from tests import oracle_pool
+    _announce(f"config {cfg} full size" + (f", {nsamp} sampled rows x all heads" if nsamp else ", compared in full"))
+    w = config(cfg)
+    t = gp.prepare(w)
+    out = gp.attn(w, t, out=_nan_out(w))
+    # the bench's operand mode for an fp16 K/V: Q's INT8 operands made in the kernel
+    qotf = None if w.kv_int8 else gp.attn(w, t, otf=2, out=_nan_out(w))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    if qotf is not None:
+        assert torch.equal(qotf, out)
+        del qotf
+    inp = oracle_inputs(w)
+    _operands_bitexact(gp, w, t, inp)
+    got_all = out.cpu().numpy()
+    if nsamp == 0:
+        ref = oracle_pool.full_output(inp)
+        ma, rf = gp.errors(got_all, ref)
+        print(f"  {w.name}: max_abs={ma:.3e} rel_fro={rf:.3e} over all {got_all.shape[0]} x {w.num_q_heads} rows")
+    else:
+        bm = _sample_rows(w, np.random.default_rng(cfg), nsamp)
+        rows = oracle_pool.tile_rows(inp, [(b, hq, m) for b, m in bm for hq in range(w.num_q_heads)])
+        ma, rf = _compare_rows(gp, inp, got_all, rows)
+        print(f"  {w.name}: max_abs={ma:.3e} rel_fro={rf:.3e} over {len(bm)} tile rows x {w.num_q_heads} heads")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+@pytest.fixture(scope="module")
+def long_context(gp):
+    """The long-context workload's inputs, uploaded once for the coverage sweep."""
+    w = config(5)
+    t = gp.upload(w)
+    inp = oracle_inputs(w)
+    return w, t, inp
+
+
+@pytest.mark.parametrize("p", [0.0, 0.25, 0.75, 1.0])
+def test_long_context_coverage_sweep_full_length(gp, long_context, p):
+    """The long-context workload (L = 65536, 32/8 heads, g = 16: 64 route groups
+    per row at full length) at INT8 coverage 0/25/75/100 % of the tile groups
+    (50 % is the standard case): NaN-initialised output finite everywhere; rows
+    0, 1, 1022, 1023, both sides of two group boundaries and a middle row, every
+    query head, against the oracle."""
+    import torch
+    from tests import oracle_pool
+    from workloads import route_bernoulli_groups
+    _announce(f"config 5 full length, coverage {p}")
+    w, t0, inp = long_context
+    tr = route_bernoulli_groups(5, w.num_kv_heads, [int(x) for x in w.lengths], w.T, w.g, p)
+    t = dict(t0, tile_route=torch.from_numpy(tr).to("cuda:0"))
+    t = gp.prepare(w, t=t)
+    out = gp.attn(w, t, out=_nan_out(w))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    inp.words = orc.build_route_mask(tr, w.cu_seqlens, w.max_seqlen, w.g)
+    assert np.array_equal(gp.words_u64(t["words"]), inp.words)
+    if p in (0.0, 1.0):
+        legal_groups = [(int(inp.words[hk, 0, m]), m // w.g + 1) for hk in range(w.num_kv_heads) for m in (1023,)]
+        assert all(wd == (0 if p == 0.0 else (1 << n) - 1) for wd, n in legal_groups)
+    ms = (0, 1, 255, 256, 511, 512, 700, 1022, 1023)
+    rows = oracle_pool.tile_rows(inp, [(0, hq, m) for m in ms for hq in range(w.num_q_heads)])
+    ma, rf = _compare_rows(gp, inp, out.cpu().numpy(), rows, label=f"p={p}")
+    print(f"  p={p}: max_abs={ma:.3e} rel_fro={rf:.3e} over {len(rows)} tile rows")
     assert ma <= MAX_ABS and rf <= REL_FRO
 
 
@@ -946,6 +1024,7 @@ def test_chunked_bench_workloads_sampled(gp, mode, nsamp):
         num += float(np.sum((got - ref) ** 2))
         den += float(np.sum(ref ** 2))
     ma, rf = max(errs), (num / den) ** 0.5
+    gp.record(ma, rf)
     print(f"  {mode}: max_abs={ma:.3e} rel_fro={rf:.3e} lse={max(lerrs):.3e} over {nsamp} rows")
     assert ma <= MAX_ABS and rf <= REL_FRO and max(lerrs) <= LSE_ABS
 
@@ -975,3 +1054,91 @@ def test_attn_strided_layouts_bitexact(gp):
         t2 = dict(t, k8=head_major(t["k8"]), v8=head_major(t["v8"]))
         assert t2["k8"].stride(0) == 128 and t2["k8"].stride(1) == int(w.cu_seqlens_k[-1]) * 128
         assert torch.equal(gp.attn(w, t2), ref)
+
+
+def _big_stride_views(k, v, stride):
+    """K and V of one KV head ([N][1][d] host arrays) placed in one device buffer
+    of `stride` elements per token (K in channels 0..d-1, V in d..2d-1): views
+    [N][1][d] whose token stride is `stride`."""
+    import torch
+    N, _, d = k.shape
+    dtype = torch.float16 if k.dtype == np.float16 else torch.int8
+    buf = torch.zeros((N, stride), dtype=dtype, device="cuda:0")
+    buf[:, :d] = torch.from_numpy(np.ascontiguousarray(k[:, 0])).to("cuda:0")
+    buf[:, d:2 * d] = torch.from_numpy(np.ascontiguousarray(v[:, 0])).to("cuda:0")
+    return buf, buf[:, None, :d], buf[:, None, d:2 * d]
+
+
+@pytest.mark.parametrize("case", ["prefill_fp16", "decode_fp16", "prefill_int8kv_gqa3"])
+def test_attn_kv_stride_beyond_4gib(gp, case):
+    """K/V tiles are read through 32-bit buffer ranges.  Here K and V are views
+    with a token stride of 4 MiB over 2100 keys, so a sequence's keys span about
+    8.8 GB while each 64-row tile spans 256 MiB: the fused prefill kernel (fp16
+    K/V, and an INT8 cache with three heads per item) and the decode kernel
+    against the oracle."""
+    import torch
+    _announce(f"attn k/v stride beyond 4 GiB: {case}")
+    L = 2100
+    if case == "decode_fp16":
+        w = make_chunked_workload(542, lengths_q=[1], lengths_k=[L], num_q_heads=3, num_kv_heads=1, head_dim=128,
+                                  g=1, p=0.5, outliers=True)
+    else:
+        w = make_workload(541, lengths=[L], num_q_heads=3, num_kv_heads=1, head_dim=128, g=1, p=0.5,
+                          outliers=True, kv_int8=case.endswith("gqa3"))
+    t = gp.prepare(w)
+    ref_out = gp.attn(w, t).clone()          # compact K/V, for the bits
+    if w.kv_int8:
+        stride = 1 << 22                       # int8 elements = bytes
+        buf, k8v, v8v = _big_stride_views(t["k8"].cpu().numpy(), t["v8"].cpu().numpy(), stride)
+        t = dict(t, k8=k8v, v8=v8v)
+        span = (L - 1) * stride + 256
+    else:
+        stride = 1 << 21                       # fp16 elements: 4 MiB per token
+        buf, kv, vv = _big_stride_views(w.k, w.v, stride)
+        t = dict(t, k=kv, v=vv)
+        span = ((L - 1) * stride + 256) * 2
+    assert span > (1 << 32) and 64 * stride * buf.element_size() < (1 << 32)
+    out = gp.attn(w, t, out=_nan_out(w))
+    torch.cuda.synchronize()
+    del buf
+    assert torch.equal(out, ref_out)         # addressing only: the same bits as the compact layout
+    ma, rf = gp.errors(out.cpu().numpy(), orc.attn_prefill(oracle_inputs(w)))
+    print(f"  max_abs={ma:.3e} rel_fro={rf:.3e}")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+
+
+@pytest.mark.parametrize("case", ["gqa3_lds_staging", "gqa2_register_staging", "decode"])
+def test_attn_kv_int8_tiny_and_zero_v_scales(gp, case):
+    """INT8 KV cache with v scales below 2^-24 and a caller-stored zero v scale.
+    The second sequence's V is ~1e-6 (its scales ~3e-8), so its output is ~1e-6
+    and only its own relative error would see a misapplied scale; one V block
+    of the first sequence has its scale set to 0 on both sides (its values then
+    count as zero, its probabilities still in the row sums)."""
+    import torch
+    _announce(f"attn INT8 cache tiny / zero v scales: {case}")
+    hq = {"gqa3_lds_staging": 6, "gqa2_register_staging": 4, "decode": 6}[case]
+    if case == "decode":
+        w = make_chunked_workload(544, lengths_q=[1, 1], lengths_k=[300, 200], num_q_heads=hq, num_kv_heads=2,
+                                  head_dim=128, g=1, p=0.5, outliers=True, kv_int8=True)
+    else:
+        w = make_workload(543, lengths=[300, 200], num_q_heads=hq, num_kv_heads=2, head_dim=128, g=1, p=0.5,
+                          outliers=True, kv_int8=True)
+    cu_k = w.cu_seqlens if w.cu_seqlens_k is None else w.cu_seqlens_k
+    s1 = int(cu_k[1])
+    w.v[s1:] = (w.v[s1:].astype(np.float32) * np.float32(1e-6)).astype(np.float16)
+    t = gp.prepare(w)
+    inp = oracle_inputs(w)
+    assert np.all(inp.v_scale[:, 1, :4] < 2.0 ** -24) and np.all(inp.v_scale[:, 1, :4] > 0)
+    t["v_s"][0, 0, 2] = 0.0
+    inp.v_scale[0, 0, 2] = 0.0
+    inp._kv_cache.clear()
+    out = gp.attn(w, t, out=_nan_out(w))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    ref = orc.attn_prefill(inp)
+    q1 = int(w.cu_seqlens[1])
+    for label, sl in (("seq0", slice(0, q1)), ("seq1 tiny v", slice(q1, None))):
+        ma, rf = gp.errors(got[sl], ref[sl], label=label)
+        print(f"  {label}: max_abs={ma:.3e} rel_fro={rf:.3e} (|ref| max {np.max(np.abs(ref[sl])):.2e})")
+        assert ma <= MAX_ABS and rf <= REL_FRO
