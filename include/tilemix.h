@@ -255,6 +255,33 @@ int32_t tilemix_attn_workspace_size(const tilemix_attn_params* params, size_t* b
 int32_t tilemix_attn_prefill(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the device array that holds tilemix_attn_prefill_noalloc's work list. */
+#define TILEMIX_NOALLOC_WORKSPACE_BYTES (4u << 20)
+
+/*
+ * tilemix_attn_prefill without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same computation, kernels and output bits
+ * as tilemix_attn_prefill; the work list goes to a file-scope device array of
+ * TILEMIX_NOALLOC_WORKSPACE_BYTES (4 MiB) that the library holds on every GPU
+ * it runs on until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).
+ *
+ * Limit: calls whose work list (tilemix_attn_workspace_size) exceeds the array
+ * are rejected with TILEMIX_ERR_WORKSPACE before any launch.  4 MiB holds
+ * about 250,000 work items (16 bytes each, plus a segment table): batch 480 of
+ * 4096 tokens with 8 KV heads and 3 query heads per KV head (245,760 items)
+ * fits; the 3B-shaped batch of 8 needs 4,096.
+ * Device and concurrency: the array of the current device is used (take the
+ * stream from that device).  Every call on one GPU shares its array and rewrites
+ * the whole work list before reading it, so calls that overlap on one GPU
+ * (several streams or threads at once) race; serialise them.
+ * Errors: as tilemix_attn_prefill, plus TILEMIX_ERR_HIP if the array's device
+ * address cannot be obtained.
+ */
+int32_t tilemix_attn_prefill_noalloc(const tilemix_attn_params* params, const tilemix_attn_tensors* tensors,
+                                     void* stream);
+
 /*
  * The varlen/GQA work schedule alone ([PL §4]: prefix-sum metadata,
  * padding-free execution): from cu_seqlens (device int32 [batch+1]; with

@@ -96,6 +96,11 @@ struct SchedArgs {
 
 WorkspaceLayout workspace_layout(int32_t batch, int32_t T, int32_t Hk, int32_t nch);
 
+// Host-side validation of an attention call's params and tensors (no HIP call).
+int32_t validate_attn_call(const tilemix_attn_params* p, const tilemix_attn_tensors* t);
+// Sets the calling thread's tilemix_last_error() text; returns status.
+int32_t set_last_error(int32_t status, const char* text);
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_build_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s);

@@ -304,6 +304,17 @@ int32_t attn_common(const tilemix_attn_params* p, const tilemix_attn_tensors* t,
 
 }  // namespace
 
+int32_t validate_attn_call(const tilemix_attn_params* p, const tilemix_attn_tensors* t) {
+  int32_t st = validate_attn_params(p);
+  if (st != TILEMIX_OK) return st;
+  return validate_tensors(p, t);
+}
+
+int32_t set_last_error(int32_t status, const char* text) {
+  g_last_error = text;
+  return status;
+}
+
 WorkspaceLayout workspace_layout(int32_t batch, int32_t T, int32_t Hk, int32_t nch) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WorkspaceLayout w;

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "TILEMIX_OK", 1: "TILEMIX_ERR_INVALID_ARG", 2: "TILEMIX_ERR_U
 EXPORTED = ("tilemix_status_string", "tilemix_last_error", "tilemix_version", "tilemix_quantize_blockwise",
             "tilemix_build_route_mask", "tilemix_decode_route_mask", "tilemix_attn_workspace_size",
             "tilemix_attn_prefill", "tilemix_attn_plan", "tilemix_attn_run", "tilemix_attn_prefill_debug",
-            "tilemix_template_route_words")
+            "tilemix_template_route_words", "tilemix_attn_prefill_noalloc")
 
 # Static routing templates (tilemix_template enum of include/tilemix.h).
 TEMPLATES = {"all_fp16": 0, "all_int8": 1, "band": 2, "global": 3, "row_random": 4, "aligned_sparse": 5,
@@ -92,6 +92,8 @@ def _load():
     lib.tilemix_attn_plan.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, sz, vp]
     lib.tilemix_attn_run.restype = i32
     lib.tilemix_attn_run.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(AttnTensors), vp, sz, vp]
+    lib.tilemix_attn_prefill_noalloc.restype = i32
+    lib.tilemix_attn_prefill_noalloc.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(AttnTensors), vp]
     lib.tilemix_attn_prefill_debug.restype = i32
     lib.tilemix_attn_prefill_debug.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(AttnTensors), vp, sz,
                                                ctypes.POINTER(Debug), vp]
@@ -315,6 +317,26 @@ def tilemix_attn_prefill(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g
         out = torch.empty((N, Hq, d), dtype=torch.float32 if out_fp32 else torch.float16, device=q.device)
     return plan.run(q, k, v, q_q, q_scale, k_q, k_scale, cu_seqlens, route_words, out, v_scale=v_scale,
                     stream=stream, cu_seqlens_k=cu_seqlens_k, lse=lse)
+
+
+def tilemix_attn_prefill_noalloc(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g: int, q_q=None,
+                                 q_scale=None, k_q=None, k_scale=None, blk_q: int = 64,
+                                 sm_scale: Optional[float] = None, kv_int8: bool = False, v_scale=None,
+                                 otf_quant: int = 0, cu_seqlens_k=None, max_seqlen_k: int = 0, lse=None,
+                                 out: torch.Tensor, stream=None) -> torch.Tensor:
+    """tilemix_attn_prefill_noalloc: the same call as tilemix_attn_prefill with no workspace (the library
+    keeps the work list in a fixed device array).  `out` (fp16 or float32 [N][Hq][d]) is the caller's; this
+    wrapper allocates nothing on the device."""
+    N, Hq, d = q.shape
+    Hk = k.shape[1]
+    B = cu_seqlens.numel() - 1
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    params = AttnProblem(B, int(max_seqlen), Hq, Hk, d, int(g), int(blk_q), float(sm_scale), bool(kv_int8),
+                         out.dtype == torch.float32, int(otf_quant), int(max_seqlen_k)).params()
+    t = _tensors(q, k, v, q_q, q_scale, k_q, k_scale, v_scale, cu_seqlens, route_words, out, cu_seqlens_k, lse)
+    _check(_lib.tilemix_attn_prefill_noalloc(ctypes.byref(params), ctypes.byref(t), _stream(stream)))
+    return out
 
 
 def tilemix_attn_prefill_debug(q, k, v, *, cu_seqlens, route_words, max_seqlen: int, g: int, q_q=None,

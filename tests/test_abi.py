@@ -215,3 +215,26 @@ def test_kv_stride_tile_span_limit(tm):
         assert lib.tilemix_attn_run(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(a), 1 << 30, None) == 2
         t.kv_stride_tok = limit - 16
         assert lib.tilemix_attn_prefill(ctypes.byref(p), ctypes.byref(t), None, 0, None) == 4
+
+
+def test_noalloc_entry_point_host_checks(tm):
+    """tilemix_attn_prefill_noalloc validates like tilemix_attn_prefill and
+    rejects, before any HIP call, a call whose work list exceeds its fixed
+    device array of 4 MiB (a batch of 480 sequences of 4096 tokens at 8 KV
+    heads, 245,760 items of 16 bytes plus the segment table, still fits)."""
+    lib = tm.lib()
+    a = 1 << 20
+    t = tm.AttnTensors(a, a, a, 24 * 128, 128, 8 * 128, 128, a, a, a, a, None, a, a, a)
+    p = _params(tm).params()
+    p.causal = 0
+    assert lib.tilemix_attn_prefill_noalloc(ctypes.byref(p), ctypes.byref(t), None) == 2
+    p = _params(tm).params()
+    t0 = tm.AttnTensors()
+    assert lib.tilemix_attn_prefill_noalloc(ctypes.byref(p), ctypes.byref(t0), None) == 1
+    # 1024 sequences x 64 query tiles x 8 KV heads x 1 chunk of 3 heads = 524,288 items: 8 MiB of work list
+    big = _params(tm, batch=1024).params()
+    need = tm.tilemix_attn_workspace_size(_params(tm, batch=1024))
+    assert need > 4 << 20
+    assert lib.tilemix_attn_prefill_noalloc(ctypes.byref(big), ctypes.byref(t), None) == 4
+    assert "no-allocation" in tm.last_error() and str(need) in tm.last_error()
+    assert tm.tilemix_attn_workspace_size(_params(tm, batch=480)) <= 4 << 20 < need
