@@ -9,7 +9,11 @@ on chip by default, so the step's quantiser call covers K only; --once
 quantises Q beforehand as well, --otf makes K's on chip too.  All three give
 the same output bits.  The step is captured once as a HIP graph and replayed
 (--eager: launched directly); the attention kernel's own time comes from HIP
-events around it in the eager steps that precede the capture.  Default workload: the LLaMA-3.2-3B-shaped attention layer
+events around it in the eager steps that precede the capture.  Before the
+warm-up steps of each phase the step runs untimed for --settle-ms of wall time
+(default 300 ms, reported in the line): the GPU raises its clocks over tens of
+milliseconds of sustained work, and a short timed window would otherwise time
+that ramp.  Default workload: the LLaMA-3.2-3B-shaped attention layer
 (batch 8, L = 4096, 24 query / 8 KV heads, d = 128, causal, FP16, 4 outlier
 channels, 64x64 tiles, g = 1, 75 % of the legal tile groups INT8).
 
@@ -103,39 +107,103 @@ def work_model(w, words):
                 ops=f_qk16 + f_qk8 + f_pv, t_star=t_star)
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """The oracle (as it stands) on a bounded sample of the same workload,
-    extrapolated to the full step by legal-tile work."""
+def _sampled_rows(inp, total_work, budget_s, seed=0):
+    """Time the oracle on random (sequence, head, query-tile) rows in this
+    process for about budget_s; returns (seconds per unit of legal-tile work, rows, work)."""
     import oracle as orc
-    from tests.oracle_inputs import oracle_inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    t0 = time.perf_counter()
-    inp = oracle_inputs(w)          # quantise Q/K(/V) and pack the route words, in full
-    t_prep = time.perf_counter() - t0
-    spans = orc.seq_spans(w.cu_seqlens)
-    total_work = sum(w.num_q_heads * t * (t + 1) // 2 for t in (orc.num_tiles(L) for _, L in spans))
-    rng = np.random.default_rng(0)
+    spans = orc.seq_spans(inp.cu)
+    rng = np.random.default_rng(seed)
     done_work, t_attn, rows = 0, 0.0, 0
     while t_attn < budget_s:
         b = int(rng.integers(len(spans)))
         Tb = orc.num_tiles(spans[b][1])
         m = int(rng.integers(Tb))
-        hq = int(rng.integers(w.num_q_heads))
+        hq = int(rng.integers(inp.Hq))
         t1 = time.perf_counter()
         orc.attn_tile_row(inp, b, hq, m)
         t_attn += time.perf_counter() - t1
         done_work += m + 1
         rows += 1
-    t_full = t_prep + t_attn * total_work / done_work
-    return {"value": w.num_tokens / t_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "host_cpus": len(os.sched_getaffinity(0)),
-            "sample": f"quantise+pack in full ({t_prep:.2f} s); attention on {rows} random (seq, head, query-tile) "
-                      f"rows ({done_work} of {total_work} legal tile visits, {t_attn:.1f} s), extrapolated by "
-                      f"legal-tile work"}
+    return t_attn / done_work, rows, done_work, t_attn
+
+
+# whole-workload oracle timing up to this much legal-tile work (the 3B layer has 399,360 units)
+FULL_ORACLE_WORK = 500_000
+
+
+def cpu_baseline(w, budget_s=15.0, budget_1t=5.0):
+    """The oracle, as it stands, timed on this host's cores.  The oracle inputs
+    (its own quantiser and packer) are made in full.  The attention is timed
+    on the whole workload when its legal-tile work is at most FULL_ORACLE_WORK
+    units: rows go to worker processes, one BLAS thread each.  Larger
+    workloads use a bounded random sample of rows, extrapolated by legal-tile
+    work.  A one-thread figure (one process, BLAS limited to one thread, a
+    sample of rows) is reported beside it."""
+    import oracle as orc
+    from tests.oracle_inputs import oracle_inputs
+    from tests import oracle_pool
+    t0 = time.perf_counter()
+    inp = oracle_inputs(w)          # quantise Q/K(/V) and pack the route words, in full
+    t_prep = time.perf_counter() - t0
+    spans = orc.seq_spans(w.cu_seqlens)
+    total_work = sum(w.num_q_heads * t * (t + 1) // 2 for t in (orc.num_tiles(L) for _, L in spans))
+    host = len(os.sched_getaffinity(0))
+    if total_work <= FULL_ORACLE_WORK:
+        procs = oracle_pool.workers()
+        t1 = time.perf_counter()
+        oracle_pool.full_output(inp, procs=procs)
+        t_attn = time.perf_counter() - t1
+        t_full = t_prep + t_attn
+        sample = (f"whole workload: quantise+pack {t_prep:.2f} s (one process), attention over all "
+                  f"{total_work} legal (sequence, head, query tile, key tile) units {t_attn:.1f} s "
+                  f"({procs} worker processes, one BLAS thread each)")
+        cores = procs
+    else:
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = 1
+        per_work, rows, done, t_attn = _sampled_rows(inp, total_work, budget_s)
+        t_full = t_prep + per_work * total_work
+        sample = (f"quantise+pack in full ({t_prep:.2f} s); attention on {rows} random (seq, head, query-tile) "
+                  f"rows ({done} of {total_work} legal tile visits, {t_attn:.1f} s), extrapolated by "
+                  f"legal-tile work")
+    res = {"value": w.num_tokens / t_full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "host_cpus": host, "sample": sample}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            per_work, rows, done, t_attn = _sampled_rows(inp, total_work, budget_1t, seed=1)
+        t1t = t_prep + per_work * total_work
+        res["one_thread"] = {"value": w.num_tokens / t1t, "unit": "tokens/s", "cores": 1,
+                             "sample": f"{rows} random rows ({done} tile visits, {t_attn:.1f} s) in one process "
+                                       f"with one BLAS thread, extrapolated by legal-tile work; "
+                                       f"quantise+pack as above"}
+    except ImportError:  # pragma: no cover
+        pass
+    return res
+
+
+def settle_clocks(step, settle_ms):
+    """Run the step untimed until the GPU has been busy for settle_ms of wall
+    time, before the warm-up steps.  The part raises its clocks over tens of
+    milliseconds of sustained work: without this, a short run (a few warm-up
+    steps, 20 timed ones) times the ramp rather than the steady state a
+    stream of layers runs at.  Returns what was run, for the JSON line."""
+    import torch
+    if settle_ms <= 0:
+        return {"ms": 0.0, "steps": 0}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()      # keep the host within a few steps of the GPU
+    torch.cuda.synchronize()
+    return {"ms": (time.perf_counter() - t0) * 1e3, "steps": n}
 
 
 def deviation_sweep(args, w, plan, q, k, v, cu, q_q, q_s, k_q, k_s, v_q, v_s, words, stream):
@@ -278,6 +346,7 @@ def chunked_bench(args):
         if ev is not None:
             ev[1].record(stream)
 
+    settle = settle_clocks(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -294,6 +363,7 @@ def chunked_bench(args):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(stream=torch.cuda.current_stream())
+        settle_graph = settle_clocks(lambda: g.replay(), args.settle_ms)
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -302,6 +372,7 @@ def chunked_bench(args):
             g.replay()
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        settle = {"eager": settle, "graph": settle_graph}
     t_attn = float(np.mean(attn_ms)) * 1e-3
     # bytes every operand once: the INT8 cache (K8, V8 and their scales), fp16 Q, its int8 copy and scales,
     # route words, fp16 output
@@ -314,7 +385,7 @@ def chunked_bench(args):
            "config": {"workload": w.name, "batch": B, "query_tokens": N, "kv_layout": args.kv_layout, "keys_per_sequence": int(w.lengths_k[0]),
                       "num_q_heads": Hq, "num_kv_heads": Hk, "head_dim": d, "int8_pair_fraction":
                       work["pairs_int8"] / work["pairs"]},
-           "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
+           "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)), "settle": settle,
            "roofline_mfma": {"achieved": work["ops"] / t_attn / 1e12, "peak": work["ops"] / work["t_star"] / 1e12,
                              "unit": "TFLOP/s", "frac": work["t_star"] / t_attn},
            "roofline_hbm": {"achieved": bytes_ / t_attn / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
@@ -349,6 +420,9 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="launch the step directly instead of replaying it as a captured HIP graph")
     ap.add_argument("--graph", action="store_true", help="(the default) replay the step as a captured HIP graph")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warm-up steps, run the step untimed for this many ms of wall time so the GPU "
+                         "clocks reach their sustained level (0: off); reported in the JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -444,6 +518,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    settle = settle_clocks(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -462,6 +537,8 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(stream=torch.cuda.current_stream())
+        # capture and instantiation leave the GPU idle: settle again before the replays
+        settle_graph = settle_clocks(lambda: g.replay(), args.settle_ms)
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -470,6 +547,7 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        settle = {"eager": settle, "graph": settle_graph}
     t_attn = float(np.mean(attn_ms)) * 1e-3
     achieved = work["ops"] / t_attn
     blended_peak = work["ops"] / work["t_star"]
@@ -493,6 +571,7 @@ def main():
         "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
         "attn_tokens_per_s": N / t_attn, "t_star_ms": work["t_star"] * 1e3,
         "hip_graph": bool(args.graph), "ms_per_step_eager": eager_ms,
+        "settle": settle,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
