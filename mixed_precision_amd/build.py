@@ -2,13 +2,17 @@
 
 Every HIP/C++ source under csrc/ is compiled to an object in parallel and the
 objects are linked into ``mixed_precision_amd/libtilemix.so``.  Always rebuilds
-(the caller decides when); objects go to ``mixed_precision_amd/_build``.
+(the caller decides when); objects go to ``mixed_precision_amd/_build``.  The
+compiler's per-kernel resource figures (VGPRs, spills, scratch, occupancy,
+LDS) are kept in ``mixed_precision_amd/kernel_resources.json``.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -48,13 +52,31 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
+RESOURCES = os.path.join(HERE, "kernel_resources.json")
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                     r"VGPRs Spill|SGPRs Spill|LDS Size \[bytes/block\]):\s+(\S+)")
+
+
+def _resources(stderr: str):
+    """Per-kernel register, spill, scratch, occupancy and LDS figures from the
+    compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for key, val in _REMARK.findall(stderr):
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split(" [")[0]] = int(val) if val.isdigit() else val
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + CXXFLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + CXXFLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) + \
+        ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(verbose: bool = True, jobs: int | None = None) -> str:
@@ -62,7 +84,13 @@ def build(verbose: bool = True, jobs: int | None = None) -> str:
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)), 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        done = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in done]
+    res = {}
+    for _, r in done:
+        res.update(r)
+    with open(RESOURCES, "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

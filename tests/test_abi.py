@@ -238,3 +238,30 @@ def test_noalloc_entry_point_host_checks(tm):
     assert lib.tilemix_attn_prefill_noalloc(ctypes.byref(big), ctypes.byref(t), None) == 4
     assert "no-allocation" in tm.last_error() and str(need) in tm.last_error()
     assert tm.tilemix_attn_workspace_size(_params(tm, batch=480)) <= 4 << 20 < need
+
+
+# Known spills of non-debug kernels (VGPRs): the full on-the-fly mode with 3 heads
+# per item at d = 128 keeps K's quantisation between two barriers beside three
+# q-blocks.
+SPILL_ALLOWANCE = {"_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2}
+
+
+def test_kernel_resources_no_new_spills(tm):
+    """The compiler's resource figures of the built library (kernel_resources.json,
+    written by the build): every attention kernel keeps two waves per SIMD, and no
+    non-debug kernel spills registers beyond the known case above."""
+    import json
+    path = os.path.join(ROOT, "mixed_precision_amd", "kernel_resources.json")
+    if not os.path.exists(path):
+        from mixed_precision_amd import build as b
+        b.build(verbose=False)
+    res = json.load(open(path))
+    attn = {k: v for k, v in res.items() if "attn_prefill_kernel" in k or "attn_decode_kernel" in k}
+    assert len(attn) >= 40
+    for name, r in attn.items():
+        assert r["Occupancy"] >= 2, (name, r)
+        debug = name.endswith("ELb1EEEvNS_8AttnArgsE") and "prefill" in name
+        if not debug:
+            assert r["VGPRs Spill"] <= SPILL_ALLOWANCE.get(name, 0), (name, r)
+    headline = attn["_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb0ELi2ELb0EEEvNS_8AttnArgsE"]
+    assert headline["VGPRs Spill"] == 0 and headline["ScratchSize"] == 0
