@@ -70,7 +70,9 @@ void attn_decode_kernel(const AttnArgs a) {
   const uint32_t k8_stride = KVI8 ? kv_stride : (uint32_t)(a.Hk * D);
   const char* k8base = KVI8 ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)kseq0 * a.Hk + hk) * D);
   auto tile_rsrc = [&](const char* base, uint32_t stride, int n, bool empty) __attribute__((always_inline)) {
-    const int rows = empty ? 0 : min(max(Lk - n * kTile, 0), kTile);
+    // (min after a readfirstlane: as one min/max pair the clamp becomes a VALU
+    // med3, and the descriptor built from it a waterfall loop per load)
+    const int rows = empty ? 0 : min(__builtin_amdgcn_readfirstlane(max(Lk - n * kTile, 0)), kTile);
     return make_rsrc(base + (int64_t)n * kTile * stride, (uint32_t)rows * stride);
   };
   typename A::Dma dma;

@@ -269,14 +269,12 @@ struct Attn {
     f16x2 s2, b2;     // 2^E and -1152 2^E for the widening fma
   };
   static TM_DEV VSplit vsplit(float vsc) {
-    int E = -24;
-    float mv = 1.0f;
-    if (vsc >= 0x1p-24f) {
-      E = min((int)((__builtin_bit_cast(uint32_t, vsc) >> 23) & 0xFF) - 127, 5);
-      mv = __builtin_ldexpf(vsc, -E);
-    } else if (vsc > 0.0f) {
-      mv = vsc * 0x1p24f;   // exact
-    }
+    // (selects, not branches: the split sits between a tile's loads and its
+    // barrier)
+    const bool big = vsc >= 0x1p-24f;
+    const int E = big ? min((int)((__builtin_bit_cast(uint32_t, vsc) >> 23) & 0xFF) - 127, 5) : -24;
+    const float tiny = vsc > 0.0f ? vsc * 0x1p24f : 1.0f;   // (exact)
+    const float mv = big ? __builtin_ldexpf(vsc, -E) : tiny;
     const float p2 = vsc > 0.0f ? __builtin_ldexpf(1.0f, E) : 0.0f;
     VSplit v;
     v.lmv = __builtin_amdgcn_logf(mv);
@@ -383,7 +381,7 @@ struct Attn {
   static TM_DEV void softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float lmv, float (&nref)[QB],
                              float (&lrow)[QB], f32x4 (&lacc)[QB], f32x4 (&O)[QB][NDB], f16x8 (&P)[QB]) {
     float lm[QB];
-    bool up = false;
+    bool up = false, upj[QB];
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       // Whole-vector bit casts: clang mis-lowers __builtin_bit_cast applied to
@@ -397,11 +395,16 @@ struct Attn {
       lm[j] = __builtin_elementwise_maximum(t1, t2);
       // lm c - m_ref > kSlack in one fma (m_ref = -inf gives +inf: a first
       // finite score always moves the reference)
-      up |= __builtin_fmaf(lm[j], cj[j], nref[j]) > kSlack;
+      upj[j] = __builtin_fmaf(lm[j], cj[j], nref[j]) > kSlack;
+      up |= upj[j];
     }
+    // With three q-blocks a wave skips the reduction of each q-block none of
+    // whose rows moved (measured faster there; slower with two).
+    constexpr bool kGate = QB == 3;
     if (__any(up)) {
 #pragma unroll
       for (int j = 0; j < QB; ++j) {
+        if (kGate && !__any(upj[j])) continue;
         float mx = lm[j];
         mx = rows4_max(mx);
         const float tmax = mx * cj[j];
@@ -410,7 +413,7 @@ struct Attn {
         const float alpha = moved ? __builtin_amdgcn_exp2f(-(nref[j] + tnew)) : 1.0f;
         nref[j] = moved ? -tnew : nref[j];
         if (KVI8) lrow[j] *= alpha;
-        if (__any(moved)) {
+        if (kGate || __any(moved)) {
           if (!KVI8) lacc[j] *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) O[j][db] *= alpha;
@@ -605,7 +608,9 @@ void attn_prefill_kernel(const AttnArgs a) {
       (KVI8 || OTF) ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)kseq0 * a.Hk + hk) * D);
   // (empty: a zero-length range, the load reads zeros and touches no memory)
   auto tile_rsrc = [&](const char* base, uint32_t stride, int n, bool empty) __attribute__((always_inline)) {
-    const int rows = empty ? 0 : min(max(Lk - n * kTile, 0), kTile);
+    // (min after a readfirstlane: as one min/max pair the clamp becomes a VALU
+    // med3, and the descriptor built from it a waterfall loop per load)
+    const int rows = empty ? 0 : min(__builtin_amdgcn_readfirstlane(max(Lk - n * kTile, 0)), kTile);
     return make_rsrc(base + (int64_t)n * kTile * stride, (uint32_t)rows * stride);
   };
   typename A::Dma dma;
