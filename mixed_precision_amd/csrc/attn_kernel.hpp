@@ -657,24 +657,28 @@ void attn_prefill_kernel(const AttnArgs a) {
     for (int db = 0; db < NDB; ++db) O[j][db] = f32x4{0, 0, 0, 0};
   }
 
+  // INT8 V: the current tile's scale split, carried from tile to tile (each
+  // tile splits the next one's scale once, early, for its widening and its
+  // softmax)
+  typename A::VSplit vcur;
+  if (KVI8) vcur = A::vsplit(vscale_row[0]);
+
   // ---- prologue: tile 0 into stage 0
   {
     typename A::Stage st;
     fetch(0, OTF ? 0 : (int)(wsh & 1), st, stA, false);
     if (KVI8 && !RAWST) {
-      const typename A::VSplit v0 = A::vsplit(vscale_row[0]);
       wait_vmem();
-      A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, v0.s2, v0.b2);
+      A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, vcur.s2, vcur.b2);
     }
   }
   wait_vmem();
   if (OTF && (wsh & 1)) A::k_partial_amax(stA, wave, lane);
   __syncthreads();
   if (RAWST) {
-    const typename A::VSplit v0 = A::vsplit(vscale_row[0]);
     typename A::Stage st;
     A::stage_from_lds(st, tid, raw);
-    A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, v0.s2, v0.b2);
+    A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, vcur.s2, vcur.b2);
     lds_barrier();
   }
 
@@ -755,10 +759,12 @@ void attn_prefill_kernel(const AttnArgs a) {
     }
     // INT8 V: this tile's scale split (mantissa into P, power of two into V)
     float lmv = 0.0f, rmv = 1.0f;
+    typename A::VSplit vn;
     if (KVI8) {
-      const typename A::VSplit vs = A::vsplit(vscale_row[n]);
-      lmv = vs.lmv;
-      rmv = vs.rmv;
+      lmv = vcur.lmv;
+      rmv = vcur.rmv;
+      // (after the last tile the stage is stored but not read)
+      vn = A::vsplit(last ? 1.0f : vscale_row[n + 1]);
     }
     if (DBG) {
 #pragma unroll
@@ -811,8 +817,6 @@ void attn_prefill_kernel(const AttnArgs a) {
       __builtin_amdgcn_s_setprio(0);
     }
     if (KVI8 && !RAWST) {
-      // (after the last tile the stage is stored but not read)
-      const typename A::VSplit vn = A::vsplit(last ? 1.0f : vscale_row[n + 1]);
       wait_vmem();
       A::stage_store(st, rnext, tid, next, next + A::KBYTES, vn.s2, vn.b2);
     }
@@ -825,7 +829,6 @@ void attn_prefill_kernel(const AttnArgs a) {
     // raised priority: the workgroup cannot start the tile before it is done,
     // and the other workgroup on the CU yields meanwhile (~1 % faster)
     if (RAWST && !last) {
-      const typename A::VSplit vn = A::vsplit(vscale_row[n + 1]);
       typename A::Stage st;
       __builtin_amdgcn_s_setprio(2);
       A::stage_from_lds(st, tid, raw);
@@ -838,6 +841,7 @@ void attn_prefill_kernel(const AttnArgs a) {
     const int adv = 1 - min(left - 1, 1);
     wsh >>= adv;
     left += adv * g - 1;
+    if (KVI8) vcur = vn;
   };
   // (LDS staging computes and refills its one stage)
   char* const st2 = RAWST ? stA : stB;
