@@ -472,32 +472,53 @@ struct Attn {
 // quantised in the kernel, or Q in the kernel and K beforehand.
 enum OtfMode : int { kOtfNone = 0, kOtfQK = 1, kOtfQ = 2 };
 
+// LDS objects of a prefill workgroup.  Two stages (K tile, then V tile) as two
+// LDS objects: with a fixed object per access the compiler can tell the loads
+// into one stage from reads of the other and does not make those reads wait
+// for the loads.
+//   INT8 KV cache, up to 2 heads per item: the next tile travels through
+//   registers (staged while the current one is computed) into the other stage.
+//   INT8 KV cache, 3 heads per item (RAWST): those 16 staging registers do not
+//   fit beside three q-blocks, so lds-loads bring the raw int8 tile into `raw`
+//   while the one stage is computed, and it is widened into the stage between
+//   two barriers.
+// On-the-fly mode: the current INT8 tile's K, and per-wave Q-block maxima.
+struct AttnLds {
+  char *stA, *stB, *raw, *k8s;
+  uint32_t* qam;
+};
+template <int D, int QB, bool KVI8, int OTFM>
+TM_DEV __attribute__((always_inline)) AttnLds attn_lds() {
+  using A = Attn<D, QB, KVI8>;
+  constexpr bool OTF = OTFM == kOtfQK;
+  constexpr bool QOTF = OTFM != kOtfNone;
+  constexpr bool RAWST = KVI8 && QB == 3;
+  constexpr int STAGE = A::KBYTES + A::VBYTES + (OTF ? 16 : 0);
+  __shared__ __attribute__((aligned(1024))) char stA[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stB[RAWST ? 16 : STAGE];
+  __shared__ __attribute__((aligned(1024))) char raw[RAWST ? A::RAW_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char k8s[OTF ? A::L8::BYTES : 16];
+  __shared__ uint32_t qam[QOTF ? 3 * 4 : 1];
+  return AttnLds{stA, stB, raw, k8s, qam};
+}
+
+// The prefill kernel: one work item (a query tile of one sequence, the query
+// heads of one chunk of a KV head's GQA group) per workgroup.
 template <int D, int QB, bool KVI8, int OTFM, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_kernel(const AttnArgs a) {
   constexpr bool OTF = OTFM == kOtfQK;    // K (and Q) quantised in the kernel
   constexpr bool QOTF = OTFM != kOtfNone; // Q quantised in the kernel
   static_assert(!(KVI8 && OTF), "on-the-fly quantisation applies to an fp16 K");
-  using A = Attn<D, QB, KVI8>;
+  using A = Attn<D, QB, KVI8>;            // tile layout, DMA and staging
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
-  // two stages (K tile, then V tile) as two LDS objects: with a fixed object
-  // per access the compiler can tell the loads into one stage from reads of
-  // the other and does not make those reads wait for the loads.
-  //   INT8 KV cache, up to 2 heads per item: the next tile travels through
-  //   registers (staged while the current one is computed) into the other stage.
-  //   INT8 KV cache, 3 heads per item (RAWST): those 16 staging registers do not
-  //   fit beside three q-blocks, so lds-loads bring the raw int8 tile into `raw`
-  //   while the one stage is computed, and it is widened into the stage between
-  //   two barriers.
   constexpr bool RAWST = KVI8 && QB == 3;
-  constexpr int STAGE = A::KBYTES + A::VBYTES + (OTF ? 16 : 0);
-  __shared__ __attribute__((aligned(1024))) char stA[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stB[RAWST ? 16 : STAGE];
-  __shared__ __attribute__((aligned(1024))) char raw[RAWST ? A::RAW_BYTES : 16];
-  // on-the-fly mode: the current INT8 tile's K, and per-wave Q-block maxima
-  __shared__ __attribute__((aligned(16))) char k8s[OTF ? A::L8::BYTES : 16];
-  __shared__ uint32_t qam[QOTF ? 3 * 4 : 1];
-
+  const AttnLds lds = attn_lds<D, QB, KVI8, OTFM>();
+  char* const stA = lds.stA;
+  char* const stB = lds.stB;
+  char* const raw = lds.raw;
+  char* const k8s = lds.k8s;
+  uint32_t* const qam = lds.qam;
   const WorkItem item = a.items[blockIdx.x];
   const int b = uniform(item.b);
   const int hk = uniform(item.hk);
@@ -506,388 +527,62 @@ void attn_prefill_kernel(const AttnArgs a) {
   // empty slot (b < 0), or an item outside the problem (work list not built
   // for these parameters): nothing to do
   if (b < 0 || b >= a.batch || hk < 0 || hk >= a.Hk || m < 0 || m >= a.T || chunk < 0 || chunk >= a.nch) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int c = lane & 15;           // query column / operand row inside a 16-block
-  const int gq = lane >> 4;          // lane group 0..3
-  const int seq0 = uniform(a.cu[b]);
-  const int L = uniform(a.cu[b + 1]) - seq0;                     // queries of this sequence
-  const int kseq0 = a.cu_k ? uniform(a.cu_k[b]) : seq0;          // its first key row
-  const int Lk = a.cu_k ? uniform(a.cu_k[b + 1]) - kseq0 : L;    // its keys
-  const int qoff = Lk - L;                                       // key position of query 0
-  const int n_last = last_key_tile(m, L, Lk);                    // last key tile of this row
-  const int h_begin = chunk * a.hc;
-  const int nh = min(a.hc, a.G - h_begin);   // heads in this chunk = q-blocks per wave
-
-  // ---- per q-block bookkeeping (recomputed where needed, not kept live)
-  auto qb_rb = [&](int j) { return (wave * nh + j) & 3; };                          // row block in tile
-  auto qb_head = [&](int j) { return hk * a.G + h_begin + ((wave * nh + j) >> 2); };
-  auto qb_row = [&](int j) { return qb_rb(j) * 16 + c; };                           // query offset in tile
-  auto qb_valid = [&](int j) { return (j < nh) && (m * kTile + qb_row(j) < L); };
-  // q-block scale times sm_scale * log2(e): the INT8 score factor is sqs * k_scale
-  // (wave-uniform values, kept in scalar registers).  Both factors are kept at
-  // or above sqrt(FLT_MIN) (kScaleFloor), so their product stays a positive
-  // normal number and a (caller-supplied) zero scale cannot turn a masked -inf
-  // into NaN; scales made by the quantiser are far above that floor.
-  constexpr float kScaleFloor = 1.0842022e-19f;
-  float sqs[QB];
-  if (!QOTF) {
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      const int blk_start = m * kTile + qb_rb(j) * 16;
-      float sq = 1.0f;
-      if (j < nh && blk_start < L)
-        sq = a.q_scale[((int64_t)qb_head(j) * a.batch + b) * a.nbq + blk_start / a.blk_q];
-      sqs[j] = sgpr_f32(__builtin_elementwise_maximum(sq * a.sm_log2, kScaleFloor));
-    }
-  }
-
-  // ---- Q operands (B = Q^T): fp16 and int8, loaded once
-  f16x8 qf[QB][NDS];
-  i32x4 q8[QB][NDS8];
-  const f16* qptr = static_cast<const f16*>(a.q);
-#pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    const int64_t tok = (int64_t)seq0 + m * kTile + qb_row(j);
-    const bool valid = qb_valid(j);
-    const int hqj = qb_head(j);
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-      qf[j][ds] = valid ? *reinterpret_cast<const f16x8*>(qptr + tok * a.q_st + (int64_t)hqj * a.q_sh + ds * 32 +
-                                                         gq * 8)
-                        : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (!QOTF) {
-#pragma unroll
-      for (int ds = 0; ds < NDS8; ++ds)
-        q8[j][ds] = valid ? *reinterpret_cast<const i32x4*>(a.q_q + (tok * a.Hq + hqj) * D + ds * 64 + gq * 16)
-                          : i32x4{0, 0, 0, 0};
-    }
-  }
-  // on-the-fly Q: max |q| over the Q block (blk_q rows of the sequence,
-  // all channels) of every head of the chunk, four partials per head.  A
-  // 64-row block is this item's query tile, whose rows the waves hold in qf:
-  // one partial per q-block (16 rows); a 128-row block is read again, one
-  // partial per wave.
-  if (QOTF && a.blk_q == kTile) {
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      if (j < nh) {
-        u16x2 mx = {0, 0};
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) mx = absmax_acc(mx, __builtin_bit_cast(u32x4, qf[j][ds]));
-        const uint32_t am = wave_max_u32(absmax_bits(mx));
-        if (lane == 0) qam[wave * nh + j] = am;   // = head * 4 + row block
-      }
-    }
-  } else if (QOTF) {
-    constexpr int CPR = D / 8;   // 16-byte chunks per row
-    const int qb0 = (m * kTile / a.blk_q) * a.blk_q;
-    const int qrows = min(a.blk_q, L - qb0);
-    for (int h = 0; h < nh; ++h) {
-      const f16* src = qptr + (int64_t)(seq0 + qb0) * a.q_st + (int64_t)(hk * a.G + h_begin + h) * a.q_sh;
-      u16x2 mx = {0, 0};
-      for (int id = tid; id < qrows * CPR; id += 256)
-        mx = absmax_acc(mx, *reinterpret_cast<const u32x4*>(src + (int64_t)(id / CPR) * a.q_st + (id % CPR) * 8));
-      const uint32_t am = wave_max_u32(absmax_bits(mx));
-      if (lane == 0) qam[h * 4 + wave] = am;
-    }
-  }
-
-  // ---- sources: this sequence's key rows of KV head hk.  Per tile the buffer
-  // base moves to the tile's first row and the range covers the tile's own
-  // rows (at most 64, fewer at the sequence end), so rows >= Lk read as zero
-  // and the 32-bit range cannot wrap (the host keeps 64 rows below 4 GiB).
-  const int64_t esz = KVI8 ? 1 : 2;
-  const char* kbase = static_cast<const char*>(a.k) + ((int64_t)kseq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
-  const char* vbase = static_cast<const char*>(a.v) + ((int64_t)kseq0 * a.kv_st + (int64_t)hk * a.kv_sh) * esz;
-  const uint32_t kv_stride = (uint32_t)(a.kv_st * esz);
-  const uint32_t k8_stride = KVI8 ? kv_stride : (uint32_t)(a.Hk * D);
-  const char* k8base =
-      (KVI8 || OTF) ? kbase : reinterpret_cast<const char*>(a.k_q + ((int64_t)kseq0 * a.Hk + hk) * D);
-  // (empty: a zero-length range, the load reads zeros and touches no memory)
-  auto tile_rsrc = [&](const char* base, uint32_t stride, int n, bool empty) __attribute__((always_inline)) {
-    // (min after a readfirstlane: as one min/max pair the clamp becomes a VALU
-    // med3, and the descriptor built from it a waterfall loop per load)
-    const int rows = empty ? 0 : min(__builtin_amdgcn_readfirstlane(max(Lk - n * kTile, 0)), kTile);
-    return make_rsrc(base + (int64_t)n * kTile * stride, (uint32_t)rows * stride);
-  };
-  typename A::Dma dma;
-  if (!KVI8) A::dma_offsets(dma, wave, lane, kv_stride, k8_stride);
-
-  const uint64_t word = uniform64(a.words[((int64_t)hk * a.batch + b) * a.T + m]);
-  const int g = a.g;
-  // per-tile scales through the scalar cache (a vector load would be counted
-  // behind the tile loads in flight, and waiting for it would wait for them)
-  typedef const __attribute__((address_space(4))) float cfloat;
-  cfloat* kscale_row = OTF ? nullptr : (cfloat*)(a.k_scale + ((int64_t)hk * a.batch + b) * a.Tk);
-  cfloat* vscale_row = KVI8 ? (cfloat*)(a.v_scale + ((int64_t)hk * a.batch + b) * a.Tk) : nullptr;
-  // Route of tile n = bit floor(n/g) of the word, tracked incrementally:
-  // bit 0 of wsh is the current tile's group, `left` counts the tiles the
-  // group still covers (groups past bit 63 shift in zeros = FP16).
-  uint64_t wsh = word;
-  int left = g;
-  // start the loads of tile n (K in its route's form, and V) into stage `sg`;
-  // INT8 KV cache: into the staging registers, or the raw int8 tile into `raw`
-  auto fetch = [&](int n, int route, typename A::Stage& st, char* sg, bool empty) __attribute__((always_inline)) {
-    if (RAWST) {
-      A::raw_dma(raw, tid, wave, tile_rsrc(kbase, kv_stride, n, empty), tile_rsrc(vbase, kv_stride, n, empty),
-                 kv_stride);
-    } else if (KVI8) {
-      A::stage_load(st, tid, tile_rsrc(kbase, kv_stride, n, empty), tile_rsrc(vbase, kv_stride, n, empty),
-                    kv_stride);
-    } else {
-      A::dma_tile(route, wave, dma, kv_stride, k8_stride, tile_rsrc(kbase, kv_stride, n, empty),
-                  tile_rsrc(k8base, k8_stride, n, empty), tile_rsrc(vbase, kv_stride, n, empty), sg,
-                  sg + A::KBYTES);
-    }
-  };
-
-  // ---- online-softmax state (log2 domain), output accumulator O^T
-  f32x4 O[QB][NDB];
-  float nref[QB], lrow[QB];   // -(reference max), row sums (INT8 V)
-  f32x4 lacc[QB];
-#pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    nref[j] = INFINITY;
-    lrow[j] = 0.0f;
-    lacc[j] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) O[j][db] = f32x4{0, 0, 0, 0};
-  }
-
-  // INT8 V: the current tile's scale split, carried from tile to tile (each
-  // tile splits the next one's scale once, early, for its widening and its
-  // softmax)
-  typename A::VSplit vcur;
-  if (KVI8) vcur = A::vsplit(vscale_row[0]);
-
-  // ---- prologue: tile 0 into stage 0
   {
-    typename A::Stage st;
-    fetch(0, OTF ? 0 : (int)(wsh & 1), st, stA, false);
-    if (KVI8 && !RAWST) {
-      wait_vmem();
-      A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, vcur.s2, vcur.b2);
-    }
+    constexpr int QE = QB;
+    using AQ = Attn<D, QE, KVI8>;
+#include "attn_prefill_item.inc"
   }
-  wait_vmem();
-  if (OTF && (wsh & 1)) A::k_partial_amax(stA, wave, lane);
-  __syncthreads();
-  if (RAWST) {
-    typename A::Stage st;
-    A::stage_from_lds(st, tid, raw);
-    A::stage_store(st, (int)(wsh & 1), tid, stA, stA + A::KBYTES, vcur.s2, vcur.b2);
-    lds_barrier();
-  }
+}
 
-  // on-the-fly Q: Q block scales and the INT8 Q operands (channels
-  // 64 ds + 16 gq .. +15 of the lane's query row).  The waves raise their
-  // priority for this block, so the other workgroup on the CU yields the issue
-  // port until the item can start its tiles (measured ~0.4 % faster).
-  if (QOTF) {
-    __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      float sq = 1.0f;
-      if (j < nh) {
-        const int hj = (wave * nh + j) >> 2;
-        sq = uniform(block_scale(max(max(qam[hj * 4], qam[hj * 4 + 1]), max(qam[hj * 4 + 2], qam[hj * 4 + 3]))));
-      }
-      sqs[j] = sgpr_f32(__builtin_elementwise_maximum(sq * a.sm_log2, kScaleFloor));
-      const float rs = __fdiv_rn(1.0f, sq);
-      const int64_t tok = (int64_t)seq0 + m * kTile + qb_row(j);
-      const bool valid = qb_valid(j);
-      const f16* src = qptr + tok * a.q_st + (int64_t)qb_head(j) * a.q_sh + gq * 16;
-#pragma unroll
-      for (int ds = 0; ds < NDS8; ++ds) {
-        if (valid) {
-          const u32x2 lo = quant8(*reinterpret_cast<const u32x4*>(src + ds * 64), sq, rs);
-          const u32x2 hi = quant8(*reinterpret_cast<const u32x4*>(src + ds * 64 + 8), sq, rs);
-          q8[j][ds] = __builtin_bit_cast(i32x4, u32x4{lo.x, lo.y, hi.x, hi.y});
-        } else {
-          q8[j][ds] = i32x4{0, 0, 0, 0};
-        }
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-  }
-
-  // Tile n: tile n+1's loads are issued first (into the other stage, last
-  // read in step n-1; after the last tile they read nothing), then tile n is
-  // computed from its stage in two 32-key halves, and the loads are awaited
-  // before the barrier.  One body serves every tile; only the QK^T path and
-  // the causal-edge mask branch (uniformly) inside it.  The loop runs two tiles
-  // per iteration so each stage is a fixed LDS object.
-  auto tile = [&](int n, const char* cur, char* next) __attribute__((always_inline)) {
-    const int rc = (int)(wsh & 1);
-    const int rnext = (left == 1) ? (int)((wsh >> 1) & 1) : rc;
-    const bool last = (n == n_last);
-    // a key of this tile may come after the tile's first query (the diagonal
-    // tile in prefill; up to two tiles on a chunk's causal edge)
-    const bool edge = n * kTile + kTile - 1 > qoff + m * kTile;
-    const char* kl = cur;
-    const char* vl = cur + A::KBYTES;
-    typename A::Stage st;
-    fetch(n + 1, OTF ? 0 : rnext, st, next, last);
-    // on-the-fly mode, INT8 tile: quantise the stage's fp16 K into k8s
-    float ksc;
-    if (OTF) {
-      ksc = 1.0f;
-      if (rc) {
-        __builtin_amdgcn_s_setprio(2);   // (the tile waits for it: the other workgroup yields)
-        ksc = uniform(A::k_tile_scale(cur));
-        A::quant_k(cur, k8s, ksc, wave, lane);
-        __builtin_amdgcn_s_setprio(0);
-        lds_barrier();
-      }
-    } else {
-      ksc = kscale_row[n];
-    }
-    // score factors, kept > 0 so a (caller-supplied) zero scale cannot turn a
-    // masked -inf into NaN
-    float cj[QB];
-    if (rc) {
-      const float kc = __builtin_elementwise_maximum(ksc, kScaleFloor);
-#pragma unroll
-      for (int j = 0; j < QB; ++j) cj[j] = sqs[j] * kc;
-    } else {
-      const float c16 = __builtin_elementwise_maximum(KVI8 ? ksc * a.sm_log2 : a.sm_log2, 1.17549435e-38f);
-#pragma unroll
-      for (int j = 0; j < QB; ++j) cj[j] = c16;
-    }
-    // INT8 V: this tile's scale split (mantissa into P, power of two into V)
-    float lmv = 0.0f, rmv = 1.0f;
-    typename A::VSplit vn;
-    if (KVI8) {
-      lmv = vcur.lmv;
-      rmv = vcur.rmv;
-      // (after the last tile the stage is stored but not read)
-      vn = A::vsplit(last ? 1.0f : vscale_row[n + 1]);
-    }
-    if (DBG) {
-#pragma unroll
-      for (int j = 0; j < QB; ++j) {
-        const int qbi = wave * nh + j;
-        if (j < nh && (qbi & 3) == 0 && lane == 0) {
-          const int64_t t = (((int64_t)b * a.Hq + qb_head(j)) * a.T + m) * a.Tk + n;
-          if (a.dbg_visits) atomicAdd(a.dbg_visits + t, 1u);
-          if (a.dbg_route) a.dbg_route[t] = (uint8_t)rc;
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      i32x4 S[QB][2];
-      // a wave issuing MFMAs gets priority, so the other wave of the SIMD runs
-      // its softmax in their shadow; QK^T, which starts the half's dependent
-      // chain, ranks highest
-      __builtin_amdgcn_s_setprio(2);
-      if (rc == 0) {
-        A::qk16(kl, h, qf, S, c, gq);
-      } else {
-        A::qk8(OTF ? k8s : kl, h, q8, S, c, gq);
-        if (DBG) {
-#pragma unroll
-          for (int j = 0; j < QB; ++j) {
-            if (j < nh && b == a.dbg_seq && qb_head(j) == a.dbg_head && m >= a.dbg_m0 && m < a.dbg_m1 && a.dbg_s32) {
-              int32_t* dst = a.dbg_s32 + ((((int64_t)(m - a.dbg_m0) * a.Tk + n) * kTile + qb_row(j)) * kTile);
-#pragma unroll
-              for (int kk = 0; kk < 2; ++kk)
-                *reinterpret_cast<i32x4*>(dst + (2 * h + kk) * 16 + gq * 4) = S[j][kk];
-            }
-          }
-        }
-        A::int_to_float_bits(S);
-      }
-      if (edge) {
-        int qpos[QB];
-#pragma unroll
-        for (int j = 0; j < QB; ++j) qpos[j] = qoff + m * kTile + qb_row(j);
-        A::mask_diag(S, n * kTile + 32 * h + 4 * gq, qpos);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      f16x8 P[QB];
-      A::softmax(S, cj, lmv, nref, lrow, lacc, O, P);
-      // P.V: above the softmax with up to two heads per item; with three it
-      // stays at 0, so only QK^T preempts (measured both ways per head count)
-      __builtin_amdgcn_s_setprio(QB == 3 ? 0 : 1);
-      A::pv(vl, h, P, O, lacc, lrow, rmv, lane);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    if (KVI8 && !RAWST) {
-      wait_vmem();
-      A::stage_store(st, rnext, tid, next, next + A::KBYTES, vn.s2, vn.b2);
-    }
-    wait_vmem();
-    // on-the-fly mode: this wave's max |k| of an INT8 next tile
-    if (OTF && rnext && !last) A::k_partial_amax(next, wave, lane);
-    __syncthreads();
-    // LDS staging: every wave is done with the stage and the raw next tile
-    // has landed; widen it into the stage (skipped after the last tile), at
-    // raised priority: the workgroup cannot start the tile before it is done,
-    // and the other workgroup on the CU yields meanwhile (~1 % faster)
-    if (RAWST && !last) {
-      typename A::Stage st;
-      __builtin_amdgcn_s_setprio(2);
-      A::stage_from_lds(st, tid, raw);
-      A::stage_store(st, rnext, tid, next, next + A::KBYTES, vn.s2, vn.b2);
-      __builtin_amdgcn_s_setprio(0);
-      lds_barrier();
-    }
-    // next tile's group, in integer arithmetic (left >= 1; a compare here
-    // became a VALU select and a readfirstlane)
-    const int adv = 1 - min(left - 1, 1);
-    wsh >>= adv;
-    left += adv * g - 1;
-    if (KVI8) vcur = vn;
-  };
-  // (LDS staging computes and refills its one stage)
-  char* const st2 = RAWST ? stA : stB;
-#pragma unroll 1
-  for (int n = 0;; n += 2) {
-    tile(n, stA, st2);
-    if (n + 1 > n_last) break;
-    tile(n + 1, st2, stA);
-    if (n + 2 > n_last) break;
-  }
-
-  // ---- epilogue: O = acc / l.  Addresses are a wave-uniform base (the tile's
-  // first row, the chunk's first head) plus 32-bit per-lane offsets, so no
-  // 64-bit address stays live from the prologue.
-  const int64_t rowhead0 = ((int64_t)seq0 + m * kTile) * a.Hq + hk * a.G + h_begin;
-  float* lse_base = a.lse ? a.lse + rowhead0 : nullptr;
-  float* out32 = static_cast<float*>(a.out) + rowhead0 * D;
-  f16* out16 = static_cast<f16*>(a.out) + rowhead0 * D;
-#pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    if (j >= nh) continue;
-    // the row's sum (every lane of the query holds all of it)
-    const float l = KVI8 ? lrow[j] : lacc[j][0];
-    const float inv = 1.0f / l;
-    if (!qb_valid(j)) continue;
-    // (row in tile) * Hq + (head in chunk)
-    const uint32_t e = (uint32_t)(qb_row(j) * a.Hq + ((wave * nh + j) >> 2));
-    // log-sum-exp of the row's scores: the state is in log2 units of the
-    // scaled scores, so LSE = (m_ref + log2 l) ln 2
-    if (lse_base && gq == 0) lse_base[e] = (__builtin_amdgcn_logf(l) - nref[j]) * 0.6931471805599453f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const f32x4 r = O[j][db] * inv;
-      const uint32_t o = e * D + db * 16 + gq * 4;
-      if (a.out_fp32) {
-        *reinterpret_cast<f32x4*>(out32 + o) = r;
-      } else {
-        f16x4 hv = {(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
-        *reinterpret_cast<f16x4*>(out16 + o) = hv;
-      }
-    }
+// Same, for GQA groups whose last head chunk is partial (the chunk size does
+// not divide G): each item runs the body for its own head count, so a partial
+// chunk's missing q-blocks are not computed on zeros.
+template <int D, int QB, bool KVI8, int OTFM, bool DBG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_prefill_mixed_kernel(const AttnArgs a) {
+  constexpr bool OTF = OTFM == kOtfQK;
+  constexpr bool QOTF = OTFM != kOtfNone;
+  static_assert(QB > 1 && !(KVI8 && OTF), "mixed head chunks need QB > 1");
+  using A = Attn<D, QB, KVI8>;
+  constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
+  constexpr bool RAWST = KVI8 && QB == 3;
+  const AttnLds lds = attn_lds<D, QB, KVI8, OTFM>();
+  char* const stA = lds.stA;
+  char* const stB = lds.stB;
+  char* const raw = lds.raw;
+  char* const k8s = lds.k8s;
+  uint32_t* const qam = lds.qam;
+  const WorkItem item = a.items[blockIdx.x];
+  const int b = uniform(item.b);
+  const int hk = uniform(item.hk);
+  const int m = uniform(item.m);
+  const int chunk = uniform(item.chunk);
+  if (b < 0 || b >= a.batch || hk < 0 || hk >= a.Hk || m < 0 || m >= a.T || chunk < 0 || chunk >= a.nch) return;
+  const int heads = min(a.hc, a.G - chunk * a.hc);
+  if (heads >= QB) {
+    constexpr int QE = QB;
+    using AQ = Attn<D, QE, KVI8>;
+#include "attn_prefill_item.inc"
+  } else if (QB == 3 && heads == 2) {
+    constexpr int QE = QB == 3 ? 2 : 1;
+    using AQ = Attn<D, QE, KVI8>;
+#include "attn_prefill_item.inc"
+  } else {
+    constexpr int QE = 1;
+    using AQ = Attn<D, QE, KVI8>;
+#include "attn_prefill_item.inc"
   }
 }
 
 template <int D, int QB, bool KVI8, int OTFM, bool DBG>
 hipError_t launch_attn_inst(const AttnArgs& a, int64_t nslots, hipStream_t s) {
+  if constexpr (QB > 1) {
+    if (a.G % a.hc != 0) {
+      hipLaunchKernelGGL((attn_prefill_mixed_kernel<D, QB, KVI8, OTFM, DBG>), dim3((unsigned)nslots), dim3(256), 0,
+                         s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_prefill_kernel<D, QB, KVI8, OTFM, DBG>), dim3((unsigned)nslots), dim3(256), 0, s, a);
   return hipGetLastError();
 }

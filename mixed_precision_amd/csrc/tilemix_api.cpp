@@ -60,13 +60,16 @@ int32_t check_groups(int32_t max_seqlen_keys, int32_t g) {
 }
 
 // Query heads per work item.  fp16 K/V: up to 3.  INT8 KV cache: 3 when the
-// GQA ratio is a multiple of 3 (the 3-head kernel stages tiles through LDS,
-// which costs a serialized widening step per tile), else 2 (tiles staged in
-// registers; a 3 + 3 + 1 split of 7 heads measured slower than 2 + 2 + 2 + 1).
+// GQA ratio is a multiple of 3 or above 4 (the 3-head kernel stages tiles
+// through LDS, a serialized widening step per tile, but each K/V tile then
+// serves more heads: 7 heads as 3 + 3 + 1 run 11 % faster than as
+// 2 + 2 + 2 + 1, 8 as 3 + 3 + 2 5 % faster than 2 + 2 + 2 + 2, 5 as 3 + 2 4 %),
+// else 2 (tiles staged in registers).  A partial last chunk runs the kernel
+// body for its own head count.
 int32_t max_heads_per_chunk(const tilemix_attn_params* p) {
   if (!p->kv_int8) return 3;
   const int32_t G = p->num_kv_heads > 0 ? p->num_q_heads / p->num_kv_heads : 1;
-  return G % 3 == 0 ? 3 : 2;
+  return G % 3 == 0 || G > 4 ? 3 : 2;
 }
 
 int32_t validate_attn_params(const tilemix_attn_params* p) {

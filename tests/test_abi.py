@@ -242,8 +242,9 @@ def test_noalloc_entry_point_host_checks(tm):
 
 # Known spills of non-debug kernels (VGPRs): the full on-the-fly mode with 3 heads
 # per item at d = 128 keeps K's quantisation between two barriers beside three
-# q-blocks.
-SPILL_ALLOWANCE = {"_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2}
+# q-blocks (also in the kernel for partial head chunks).
+SPILL_ALLOWANCE = {"_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2,
+                   "_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2}
 
 
 def test_kernel_resources_no_new_spills(tm):
@@ -256,8 +257,9 @@ def test_kernel_resources_no_new_spills(tm):
         from mixed_precision_amd import build as b
         b.build(verbose=False)
     res = json.load(open(path))
-    attn = {k: v for k, v in res.items() if "attn_prefill_kernel" in k or "attn_decode_kernel" in k}
-    assert len(attn) >= 40
+    attn = {k: v for k, v in res.items()
+            if "attn_prefill_kernel" in k or "attn_prefill_mixed_kernel" in k or "attn_decode_kernel" in k}
+    assert len(attn) >= 80
     for name, r in attn.items():
         assert r["Occupancy"] >= 2, (name, r)
         debug = name.endswith("ELb1EEEvNS_8AttnArgsE") and "prefill" in name
@@ -265,3 +267,6 @@ def test_kernel_resources_no_new_spills(tm):
             assert r["VGPRs Spill"] <= SPILL_ALLOWANCE.get(name, 0), (name, r)
     headline = attn["_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb0ELi2ELb0EEEvNS_8AttnArgsE"]
     assert headline["VGPRs Spill"] == 0 and headline["ScratchSize"] == 0
+    # the INT8-cache kernel of three heads per item (chunked prefill) sits at the limit
+    kv8 = attn["_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb1ELi0ELb0EEEvNS_8AttnArgsE"]
+    assert kv8["VGPRs Spill"] == 0 and kv8["ScratchSize"] == 0

@@ -216,6 +216,11 @@ SMALL = [
     # INT8 KV cache with a GQA ratio of 3: three heads per item, tiles staged through LDS
     ("kv_int8_gqa3_lds", [300, 64, 130, 1], 6, 2, 128, 2, "bernoulli", 0.5, True, 64, True),
     ("kv_int8_gqa3_d64", [200, 77], 3, 1, 64, 1, "bernoulli", 0.6, True, 128, False),
+    # partial head chunks (the chunk size does not divide G): 3 + 2 and 3 + 3 + 2 heads,
+    # and 3 + 2 with the INT8 cache (tiles staged through LDS)
+    ("gqa5_chunks_3_2", [300, 129, 1], 5, 1, 128, 1, "bernoulli", 0.5, False, 64, True),
+    ("gqa8_d64_chunks_3_3_2", [260, 70], 16, 2, 64, 2, "bernoulli", 0.6, False, 128, True),
+    ("kv_int8_gqa5_chunks_3_2", [400, 65], 5, 1, 128, 2, "bernoulli", 0.5, True, 64, True),
 ]
 
 
@@ -248,7 +253,7 @@ def test_attn_small_full(gp, case):
             assert np.max(np.abs(got[s0, h] - v0)) <= 1e-3 * max(1.0, np.max(np.abs(v0)))
 
 
-@pytest.mark.parametrize("case", ["tiny", "gqa3_varlen", "kv_int8", "kv_int8_gqa3"])
+@pytest.mark.parametrize("case", ["tiny", "gqa3_varlen", "kv_int8", "kv_int8_last_chunk", "kv_int8_gqa3"])
 def test_attn_debug_bitexact(gp, case):
     """INT32 score tiles bit-exact; every legal tile visited once, nothing else;
     the decoded route per visited tile equals the oracle's."""
@@ -261,10 +266,11 @@ def test_attn_debug_bitexact(gp, case):
         w = make_workload(450, lengths=[130, 300, 64], num_q_heads=6, num_kv_heads=2, head_dim=128, g=2,
                           p=0.6, outliers=True)
         seq, head = 1, 4
-    elif case == "kv_int8":
+    elif case in ("kv_int8", "kv_int8_last_chunk"):
+        # GQA 7 in chunks of 3 + 3 + 1 heads; head 6 is the partial chunk's
         w = make_workload(451, lengths=[260, 90], num_q_heads=7, num_kv_heads=1, head_dim=128, g=1, p=0.5,
                           kv_int8=True)
-        seq, head = 0, 5
+        seq, head = (0, 5) if case == "kv_int8" else (1, 6)
     else:   # three heads per item: the INT8 tiles are staged through LDS
         w = make_workload(452, lengths=[200, 70], num_q_heads=3, num_kv_heads=1, head_dim=128, g=1, p=0.5,
                           kv_int8=True, outliers=True)
