@@ -40,10 +40,12 @@ P_INT8 = 5033.2e12        # OP/s
 HBM_PEAK = 8.0e12         # B/s
 
 
-# what decides the attention kernel's code on this workload: its header, the
-# file that instantiates it at 3 heads per work item, and the build flags
-KERNEL_SOURCES = ("mixed_precision_amd/csrc/attn_kernel.hpp", "mixed_precision_amd/csrc/attn_d128_qb3.hip",
-                  "mixed_precision_amd/build.py")
+# what decides the attention kernel's code on this workload: its headers and
+# item body, the file that instantiates it at 3 heads per work item, and the
+# build flags
+KERNEL_SOURCES = ("mixed_precision_amd/csrc/attn_kernel.hpp", "mixed_precision_amd/csrc/attn_prefill_item.inc",
+                  "mixed_precision_amd/csrc/device_common.hpp", "mixed_precision_amd/csrc/internal.hpp",
+                  "mixed_precision_amd/csrc/attn_d128_qb3.hip", "mixed_precision_amd/build.py")
 
 
 def kernel_source_digest():
@@ -68,6 +70,16 @@ def measured_traffic(workload_name):
     if not h or not t or h.group(1) != kernel_source_digest():
         return None
     return int(t.group(1))
+
+
+def attn_kernel_name(G, kv_int8):
+    """The prefill kernel the library launches for a GQA ratio: query heads go to
+    work items in chunks of up to 3 (INT8 cache: 2 when G is 4 or less and not a
+    multiple of 3), and a partial last chunk selects the mixed-chunk kernel."""
+    cap = 3 if (not kv_int8 or G % 3 == 0 or G > 4) else 2
+    nch = -(-G // cap)
+    hc = -(-G // nch)
+    return "attn_prefill_mixed_kernel" if hc > 1 and G % hc else "attn_prefill_kernel"
 
 
 def legal_pairs(lengths):
@@ -566,7 +578,7 @@ def main():
                      "frac": achieved / blended_peak,
                      "traffic": measured_traffic(w.name) if mode == 2 else None,
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
-                     "kernel": "attn_prefill_kernel",
+                     "kernel": attn_kernel_name(Hq // Hk, w.kv_int8),
                      "note": "peak = blended MFMA peak of this launch's mix: ops / (F_qk16/P16 + F_qk8/P8 + F_pv/P16)"},
         "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
         "attn_tokens_per_s": N / t_attn, "t_star_ms": work["t_star"] * 1e3,
