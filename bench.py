@@ -577,7 +577,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / blended_peak,
                      "traffic": measured_traffic(w.name) if mode == 2 else None,
-                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated), read from "
+                                     "the committed rocprofv3 counter summary profiles/attn_prefill_kernel_llama3b_B8_"
+                                     "L4096_hbm_bytes.md while its kernel-source digest matches the sources (else null)",
                      "kernel": attn_kernel_name(Hq // Hk, w.kv_int8),
                      "note": "peak = blended MFMA peak of this launch's mix: ops / (F_qk16/P16 + F_qk8/P8 + F_pv/P16)"},
         "attn_ms": float(np.mean(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
