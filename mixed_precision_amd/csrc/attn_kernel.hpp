@@ -398,9 +398,10 @@ struct Attn {
       upj[j] = __builtin_fmaf(lm[j], cj[j], nref[j]) > kSlack;
       up |= upj[j];
     }
-    // With three q-blocks a wave skips the reduction of each q-block none of
-    // whose rows moved (measured faster there; slower with two).
-    constexpr bool kGate = QB == 3;
+    // A wave skips the reduction of each q-block none of whose rows moved
+    // (measured faster with three q-blocks and with two over an fp16 cache;
+    // slower with two over the INT8 cache).
+    constexpr bool kGate = QB == 3 || (QB == 2 && !KVI8);
     if (__any(up)) {
 #pragma unroll
       for (int j = 0; j < QB; ++j) {
