@@ -543,7 +543,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_mixed_kernel(const AttnArgs a) {
   constexpr bool OTF = OTFM == kOtfQK;
   constexpr bool QOTF = OTFM != kOtfNone;
-  static_assert(QB > 1 && !(KVI8 && OTF), "mixed head chunks need QB > 1");
+  static_assert(!(KVI8 && OTF), "on-the-fly quantisation applies to an fp16 K");
+  static_assert(QB > 1, "a one-head chunk is never partial");
   using A = Attn<D, QB, KVI8>;
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
   constexpr bool RAWST = KVI8 && QB == 3;
@@ -564,7 +565,7 @@ void attn_prefill_mixed_kernel(const AttnArgs a) {
     constexpr int QE = QB;
     using AQ = Attn<D, QE, KVI8>;
 #include "attn_prefill_item.inc"
-  } else if (QB == 3 && heads == 2) {
+  } else if (QB == 3 && heads == 2) {   // (dead code at QB = 2, which the QE below keeps compilable)
     constexpr int QE = QB == 3 ? 2 : 1;
     using AQ = Attn<D, QE, KVI8>;
 #include "attn_prefill_item.inc"

@@ -650,6 +650,8 @@ CHUNKED = [
     # decode with more query heads per KV head than one 16-row block: the fused
     # prefill kernel takes it (7 items of 3 heads, one query row each)
     ("decode_gqa20_int8kv", [1] * 3, [5, 640, 2500], 20, 1, 128, 2, 0.5, True, 64),
+    # chunked prefill with a partial head chunk (GQA 5 in chunks of 3 + 2), also on the fly
+    ("chunk_gqa5_fp16kv_chunks_3_2", [150, 70, 1], [700, 70, 300], 5, 1, 128, 2, 0.5, False, 64),
 ]
 
 
