@@ -503,10 +503,21 @@ TM_DEV __attribute__((always_inline)) AttnLds attn_lds() {
   return AttnLds{stA, stB, raw, k8s, qam};
 }
 
+// Waves per SIMD each prefill kernel is built for.  d = 128: 2 (three
+// q-blocks take 248 of 256 VGPRs, and the K/V stages 67 KB of LDS).  d = 64
+// (34-38 KB of LDS): 3 with three q-blocks, or two over the INT8 cache, which
+// fit 168 VGPRs; 4 with fewer (128 VGPRs).  From 2, 3 waves per SIMD took the
+// d = 64 kernels 13-15 % less time, 4 another 5-8 %.
+template <int D, int QB, bool KVI8>
+constexpr int attn_waves_per_simd() {
+  return D == 128 ? 2 : (QB == 3 || (QB == 2 && KVI8)) ? 3 : 4;
+}
+
 // The prefill kernel: one work item (a query tile of one sequence, the query
 // heads of one chunk of a KV head's GQA group) per workgroup.
 template <int D, int QB, bool KVI8, int OTFM, bool DBG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<D, QB, KVI8>(),
+                                                                     attn_waves_per_simd<D, QB, KVI8>())))
 void attn_prefill_kernel(const AttnArgs a) {
   constexpr bool OTF = OTFM == kOtfQK;    // K (and Q) quantised in the kernel
   constexpr bool QOTF = OTFM != kOtfNone; // Q quantised in the kernel
@@ -539,7 +550,8 @@ void attn_prefill_kernel(const AttnArgs a) {
 // not divide G): each item runs the body for its own head count, so a partial
 // chunk's missing q-blocks are not computed on zeros.
 template <int D, int QB, bool KVI8, int OTFM, bool DBG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<D, QB, KVI8>(),
+                                                                     attn_waves_per_simd<D, QB, KVI8>())))
 void attn_prefill_mixed_kernel(const AttnArgs a) {
   constexpr bool OTF = OTFM == kOtfQK;
   constexpr bool QOTF = OTFM != kOtfNone;

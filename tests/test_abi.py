@@ -241,10 +241,13 @@ def test_noalloc_entry_point_host_checks(tm):
 
 
 # Known spills of non-debug kernels (VGPRs): the full on-the-fly mode with 3 heads
-# per item at d = 128 keeps K's quantisation between two barriers beside three
-# q-blocks (also in the kernel for partial head chunks).
+# per item keeps K's quantisation between two barriers beside three q-blocks: at
+# d = 128 (also in the kernel for partial head chunks), and at d = 64 in the
+# kernel for partial head chunks, whose three item bodies share the 168 VGPRs
+# of three waves per SIMD.
 SPILL_ALLOWANCE = {"_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2,
-                   "_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2}
+                   "_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2,
+                   "_ZN7tilemix25attn_prefill_mixed_kernelILi64ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 8}
 
 
 def test_kernel_resources_no_new_spills(tm):
@@ -262,6 +265,8 @@ def test_kernel_resources_no_new_spills(tm):
     assert len(attn) >= 80
     for name, r in attn.items():
         assert r["Occupancy"] >= 2, (name, r)
+        if "prefill" in name and "Li64E" in name:   # d = 64: 3 or 4 waves per SIMD
+            assert r["Occupancy"] >= 3, (name, r)
         debug = name.endswith("ELb1EEEvNS_8AttnArgsE") and "prefill" in name
         if not debug:
             assert r["VGPRs Spill"] <= SPILL_ALLOWANCE.get(name, 0), (name, r)
