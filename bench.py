@@ -412,6 +412,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--p", type=float, default=None, help="INT8 coverage override (configs 2, 4, 5)")
+    ap.add_argument("--head-dim", type=int, default=None, choices=[64, 128],
+                    help="re-shape configs 2-5 to this head dimension (same lengths, heads, routes, seeds)")
     ap.add_argument("--otf", action="store_true",
                     help="on-the-fly quantisation: Q/K INT8 operands made inside the attention kernel "
                          "(no quantiser calls in the step)")
@@ -464,7 +466,7 @@ def main():
     from workloads import config
 
     dev = torch.device("cuda:0")
-    w = config(args.config, p=args.p)
+    w = config(args.config, p=args.p, head_dim=args.head_dim)
     q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     tr = torch.from_numpy(w.tile_route).to(dev)

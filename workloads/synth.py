@@ -252,8 +252,19 @@ def varlen_lengths(cfg_id: int, count: int = 16, lo: int = 512, hi: int = 8192):
 # (LLaMA-3.2-3B-shaped layer at 4K, batch 8) and of the features the pages list
 # (GQA, unpadded varlen, INT8 KV cache, long context).
 
-def config(cfg_id: int, *, p: Optional[float] = None, scale_down: int = 1) -> Workload:
-    """Standard workload `cfg_id` in 1..5.  `scale_down` > 1 shrinks lengths (tests only)."""
+def config(cfg_id: int, *, p: Optional[float] = None, scale_down: int = 1, head_dim: Optional[int] = None) -> Workload:
+    """Standard workload `cfg_id` in 1..5.  `scale_down` > 1 shrinks lengths (tests only).
+    `head_dim` re-shapes configs 2-5 to another head dimension (same lengths, heads,
+    routes and seeds; the name's d128 becomes d<head_dim>)."""
+    if head_dim is not None and head_dim != 128 and cfg_id != 1:
+        w = config(cfg_id, p=p, scale_down=scale_down)
+        kw = dict(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=head_dim, g=w.g,
+                  outliers=cfg_id != 4, kv_int8=w.kv_int8, name=w.name.replace("_d128_", f"_d{head_dim}_"))
+        if cfg_id == 3:
+            lens = [int(x) for x in np.diff(w.cu_seqlens)]
+            return make_workload(3, lengths=lens, route="band_sink", **kw)
+        return make_workload(cfg_id, lengths=[int(x) for x in np.diff(w.cu_seqlens)], route="bernoulli",
+                             p=(0.75 if cfg_id == 2 else 0.5) if p is None else p, **kw)
     if cfg_id == 1:
         return make_workload(1, lengths=[512 // scale_down], num_q_heads=1, num_kv_heads=1, head_dim=64,
                              g=1, route="bernoulli", p=0.5 if p is None else p,
