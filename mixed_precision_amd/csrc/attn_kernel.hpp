@@ -185,6 +185,23 @@ struct Attn {
     for (int i = 0; i < NI16; ++i) bload16_lds(rv, o.b16 + i * s16, vl + (wave * NI16 + i) * LV::BLOCK);
   }
 
+  // --- the same loads, K and V apart (single V stage: V's loads are issued
+  // later than K's)
+  static TM_DEV void dma_k(int route, int wave, const Dma& o, uint32_t s16, uint32_t s8, __amdgpu_buffer_rsrc_t rk16,
+                           __amdgpu_buffer_rsrc_t rk8, char* kl) {
+    if (route == 0) {
+#pragma unroll
+      for (int i = 0; i < NI16; ++i) bload16_lds(rk16, o.b16 + i * s16, kl + (wave * NI16 + i) * L16::BLOCK);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI8; ++i) bload16_lds(rk8, o.b8 + i * s8, kl + (wave * NI8 + i) * L8::BLOCK);
+    }
+  }
+  static TM_DEV void dma_v(int wave, const Dma& o, uint32_t s16, __amdgpu_buffer_rsrc_t rv, char* vl) {
+#pragma unroll
+    for (int i = 0; i < NI16; ++i) bload16_lds(rv, o.b16 + i * s16, vl + (wave * NI16 + i) * LV::BLOCK);
+  }
+
   // --- on-the-fly K quantisation.  Load i of wave w fills LDS block
   // w*NI16 + i of the stage's K; its lane l holds channels 8 (l % (RB16/16))
   // .. +7 of row w*NI16 + i + NB (16 l / RB16), at block + 16 l.  A wave can
@@ -473,6 +490,31 @@ struct Attn {
 // quantised in the kernel, or Q in the kernel and K beforehand.
 enum OtfMode : int { kOtfNone = 0, kOtfQK = 1, kOtfQ = 2 };
 
+// Waves per SIMD each prefill kernel is built for.  d = 64 (34-38 KB of LDS):
+// 3 with three q-blocks, or two over the INT8 cache, which fit 168 VGPRs; 4
+// with fewer (128 VGPRs).  From 2, 3 waves per SIMD took the d = 64 kernels
+// 13-15 % less time, 4 another 5-8 %.  d = 128: three q-blocks take 248 of 256
+// VGPRs, so 2.  With one or two q-blocks over an fp16 cache and Q's operands
+// made in the kernel, 3 (single V stage, below); otherwise 2, because the
+// double-buffered K/V stages take 67 KB of LDS.
+//
+// Single V stage: K stays double-buffered but V gets one stage, so a
+// workgroup takes 50 KB of LDS and three fit a CU.  Tile n+1's V loads are
+// issued after the end-of-tile barrier (every wave is done with tile n's V)
+// and awaited, behind a second barrier, just before the first P.V of tile
+// n+1, i.e. behind half a tile of QK^T and softmax; the third workgroup
+// covers the rest.  The two-head kernel then spills 3 VGPRs at 168 and
+// still runs 5-8 % faster; with quantise-once operands it spilled 14 and ran
+// 3 % slower, so that mode keeps two stages.
+template <int D, int QB, bool KVI8, int OTFM>
+constexpr bool attn_single_v() {
+  return D == 128 && QB <= 2 && !KVI8 && OTFM == kOtfQ;
+}
+template <int D, int QB, bool KVI8, int OTFM>
+constexpr int attn_waves_per_simd() {
+  return D == 128 ? (attn_single_v<D, QB, KVI8, OTFM>() ? 3 : 2) : (QB == 3 || (QB == 2 && KVI8)) ? 3 : 4;
+}
+
 // LDS objects of a prefill workgroup.  Two stages (K tile, then V tile) as two
 // LDS objects: with a fixed object per access the compiler can tell the loads
 // into one stage from reads of the other and does not make those reads wait
@@ -496,28 +538,19 @@ TM_DEV __attribute__((always_inline)) AttnLds attn_lds() {
   constexpr bool RAWST = KVI8 && QB == 3;
   constexpr int STAGE = A::KBYTES + A::VBYTES + (OTF ? 16 : 0);
   __shared__ __attribute__((aligned(1024))) char stA[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stB[RAWST ? 16 : STAGE];
+  constexpr bool VS1 = attn_single_v<D, QB, KVI8, OTFM>();
+  __shared__ __attribute__((aligned(1024))) char stB[RAWST ? 16 : VS1 ? A::KBYTES : STAGE];
   __shared__ __attribute__((aligned(1024))) char raw[RAWST ? A::RAW_BYTES : 16];
   __shared__ __attribute__((aligned(16))) char k8s[OTF ? A::L8::BYTES : 16];
   __shared__ uint32_t qam[QOTF ? 3 * 4 : 1];
   return AttnLds{stA, stB, raw, k8s, qam};
 }
 
-// Waves per SIMD each prefill kernel is built for.  d = 128: 2 (three
-// q-blocks take 248 of 256 VGPRs, and the K/V stages 67 KB of LDS).  d = 64
-// (34-38 KB of LDS): 3 with three q-blocks, or two over the INT8 cache, which
-// fit 168 VGPRs; 4 with fewer (128 VGPRs).  From 2, 3 waves per SIMD took the
-// d = 64 kernels 13-15 % less time, 4 another 5-8 %.
-template <int D, int QB, bool KVI8>
-constexpr int attn_waves_per_simd() {
-  return D == 128 ? 2 : (QB == 3 || (QB == 2 && KVI8)) ? 3 : 4;
-}
-
 // The prefill kernel: one work item (a query tile of one sequence, the query
 // heads of one chunk of a KV head's GQA group) per workgroup.
 template <int D, int QB, bool KVI8, int OTFM, bool DBG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<D, QB, KVI8>(),
-                                                                     attn_waves_per_simd<D, QB, KVI8>())))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<D, QB, KVI8, OTFM>(),
+                                                                     attn_waves_per_simd<D, QB, KVI8, OTFM>())))
 void attn_prefill_kernel(const AttnArgs a) {
   constexpr bool OTF = OTFM == kOtfQK;    // K (and Q) quantised in the kernel
   constexpr bool QOTF = OTFM != kOtfNone; // Q quantised in the kernel
@@ -525,6 +558,7 @@ void attn_prefill_kernel(const AttnArgs a) {
   using A = Attn<D, QB, KVI8>;            // tile layout, DMA and staging
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
   constexpr bool RAWST = KVI8 && QB == 3;
+  constexpr bool VS1 = attn_single_v<D, QB, KVI8, OTFM>();
   const AttnLds lds = attn_lds<D, QB, KVI8, OTFM>();
   char* const stA = lds.stA;
   char* const stB = lds.stB;
@@ -550,8 +584,8 @@ void attn_prefill_kernel(const AttnArgs a) {
 // not divide G): each item runs the body for its own head count, so a partial
 // chunk's missing q-blocks are not computed on zeros.
 template <int D, int QB, bool KVI8, int OTFM, bool DBG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<D, QB, KVI8>(),
-                                                                     attn_waves_per_simd<D, QB, KVI8>())))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<D, QB, KVI8, OTFM>(),
+                                                                     attn_waves_per_simd<D, QB, KVI8, OTFM>())))
 void attn_prefill_mixed_kernel(const AttnArgs a) {
   constexpr bool OTF = OTFM == kOtfQK;
   constexpr bool QOTF = OTFM != kOtfNone;
@@ -560,6 +594,7 @@ void attn_prefill_mixed_kernel(const AttnArgs a) {
   using A = Attn<D, QB, KVI8>;
   constexpr int NDS = A::NDS, NDS8 = A::NDS8, NDB = A::NDB;
   constexpr bool RAWST = KVI8 && QB == 3;
+  constexpr bool VS1 = attn_single_v<D, QB, KVI8, OTFM>();
   const AttnLds lds = attn_lds<D, QB, KVI8, OTFM>();
   char* const stA = lds.stA;
   char* const stB = lds.stB;
