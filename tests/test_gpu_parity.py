@@ -652,6 +652,8 @@ CHUNKED = [
     ("decode_gqa20_int8kv", [1] * 3, [5, 640, 2500], 20, 1, 128, 2, 0.5, True, 64),
     # chunked prefill with a partial head chunk (GQA 5 in chunks of 3 + 2), also on the fly
     ("chunk_gqa5_fp16kv_chunks_3_2", [150, 70, 1], [700, 70, 300], 5, 1, 128, 2, 0.5, False, 64),
+    # two heads per item at d = 128: with Q on the fly, V through a single LDS stage
+    ("chunk_gqa2_fp16kv_single_v", [190, 64, 1, 129], [900, 64, 300, 1500], 4, 2, 128, 2, 0.5, False, 64),
 ]
 
 
