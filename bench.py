@@ -49,11 +49,23 @@ KERNEL_SOURCES = ("mixed_precision_amd/csrc/attn_kernel.hpp", "mixed_precision_a
 
 
 def kernel_source_digest():
+    return source_digest(KERNEL_SOURCES)
+
+
+def source_digest(files):
+    """sha256 over sources: C++ files without their // comments and blank lines
+    (an edit of a comment leaves the code, and so the counters taken on it,
+    valid), Python files as they are."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in files:
         with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+            data = f.read()
+        if not rel.endswith(".py"):
+            lines = (re.sub(rb"\s*//.*$", b"", ln).rstrip() for ln in data.split(b"\n"))
+            data = b"\n".join(ln for ln in lines if ln)
+        h.update(data)
     return h.hexdigest()
 
 

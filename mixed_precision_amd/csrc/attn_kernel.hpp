@@ -525,6 +525,8 @@ constexpr int attn_waves_per_simd() {
 //   fit beside three q-blocks, so lds-loads bring the raw int8 tile into `raw`
 //   while the one stage is computed, and it is widened into the stage between
 //   two barriers.
+//   Single V stage (attn_single_v): stage A holds K and the one V, stage B K
+//   only.
 // On-the-fly mode: the current INT8 tile's K, and per-wave Q-block maxima.
 struct AttnLds {
   char *stA, *stB, *raw, *k8s;
