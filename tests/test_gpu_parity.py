@@ -221,6 +221,9 @@ SMALL = [
     ("gqa5_chunks_3_2", [300, 129, 1], 5, 1, 128, 1, "bernoulli", 0.5, False, 64, True),
     ("gqa8_d64_chunks_3_3_2", [260, 70], 16, 2, 64, 2, "bernoulli", 0.6, False, 128, True),
     ("kv_int8_gqa5_chunks_3_2", [400, 65], 5, 1, 128, 2, "bernoulli", 0.5, True, 64, True),
+    # one and two heads per item at d = 128: with Q on the fly, V through a single LDS stage
+    ("mha_d128_single_v", [200, 65, 1], 2, 2, 128, 2, "bernoulli", 0.5, False, 64, True),
+    ("gqa2_d128_blkq128_single_v", [300, 129], 4, 2, 128, 1, "bernoulli", 0.6, False, 128, True),
 ]
 
 
