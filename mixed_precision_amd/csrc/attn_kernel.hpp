@@ -120,6 +120,11 @@ struct Attn {
   // absolute step is 2^-24.  With near one-hot rows (outlier channels) an
   // overshoot of 8 doubled the worst output error; 4 left it unchanged.
   static constexpr float kOver = 4.0f;
+  // Row sums: with three q-blocks over an fp16 cache, one all-ones MFMA per
+  // q-block and half accumulates them in a 4-register accumulator (lacc);
+  // otherwise each half's sum, from a transient MFMA result, is added to one
+  // register per q-block (lrow), 3 fewer registers per q-block.
+  static constexpr bool kLacc = !KVI8 && QB == 3;
   static constexpr int NDS = D / 32;       // fp16 MFMA k-steps over d
   static constexpr int NDS8 = D / 64;      // int8 MFMA k-steps over d
   static constexpr int NDB = D / 16;       // 16-row blocks of d in O^T
@@ -391,8 +396,9 @@ struct Attn {
   // rescale l and the accumulator (the same decision as reducing first, since
   // the reduced max exceeds the bound exactly when some lane's max does).
   // Row sums on the MFMA: an all-ones A operand times P^T gives, in every row,
-  // the query's sum over the half's 32 keys.  fp16 V accumulates it into lacc;
-  // INT8 V adds it, divided by the tile's mv, to lrow (see VSplit).
+  // the query's sum over the half's 32 keys.  kLacc accumulates it into lacc;
+  // otherwise it is added to lrow (INT8 V: divided by the tile's mv, see
+  // VSplit).
   // The reference max is kept negated (nref = -m_ref) so that every exponent
   // is one fma with it as the addend.
   static TM_DEV void softmax(const i32x4 (&S)[QB][2], const float (&cj)[QB], float lmv, float (&nref)[QB],
@@ -430,9 +436,9 @@ struct Attn {
         const float tnew = tmax + kOver;
         const float alpha = moved ? __builtin_amdgcn_exp2f(-(nref[j] + tnew)) : 1.0f;
         nref[j] = moved ? -tnew : nref[j];
-        if (KVI8) lrow[j] *= alpha;
+        if (!kLacc) lrow[j] *= alpha;
         if (kGate || __any(moved)) {
-          if (!KVI8) lacc[j] *= alpha;
+          if (kLacc) lacc[j] *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) O[j][db] *= alpha;
         }
@@ -476,7 +482,7 @@ struct Attn {
     const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
-      if (!KVI8) {
+      if (kLacc) {
         lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[j], lacc[j], 0, 0, 0);
       } else {
         const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[j], f32x4{0, 0, 0, 0}, 0, 0, 0);
@@ -494,21 +500,23 @@ enum OtfMode : int { kOtfNone = 0, kOtfQK = 1, kOtfQ = 2 };
 // 3 with three q-blocks, or two over the INT8 cache, which fit 168 VGPRs; 4
 // with fewer (128 VGPRs).  From 2, 3 waves per SIMD took the d = 64 kernels
 // 13-15 % less time, 4 another 5-8 %.  d = 128: three q-blocks take 248 of 256
-// VGPRs, so 2.  With one or two q-blocks over an fp16 cache and Q's operands
-// made in the kernel, 3 (single V stage, below); otherwise 2, because the
-// double-buffered K/V stages take 67 KB of LDS.
+// VGPRs, so 2.  With one or two q-blocks over an fp16 cache, 3 (single V
+// stage, below), except with K quantised in the kernel (its INT8 K tile needs
+// 8 KB more LDS); otherwise 2, because the double-buffered K/V stages take
+// 67 KB of LDS.
 //
 // Single V stage: K stays double-buffered but V gets one stage, so a
 // workgroup takes 50 KB of LDS and three fit a CU.  Tile n+1's V loads are
 // issued after the end-of-tile barrier (every wave is done with tile n's V)
 // and awaited, behind a second barrier, just before the first P.V of tile
 // n+1, i.e. behind half a tile of QK^T and softmax; the third workgroup
-// covers the rest.  The two-head kernel then spills 3 VGPRs at 168 and
-// still runs 5-8 % faster; with quantise-once operands it spilled 14 and ran
-// 3 % slower, so that mode keeps two stages.
+// covers the rest.  The two-head kernel fits 168 VGPRs with Q's operands made
+// in the kernel (row sums in one register per q-block, Attn::kLacc) and
+// spills 7 with quantise-once operands; both run faster than with two stages
+// (5-10 %).
 template <int D, int QB, bool KVI8, int OTFM>
 constexpr bool attn_single_v() {
-  return D == 128 && QB <= 2 && !KVI8 && OTFM == kOtfQ;
+  return D == 128 && QB <= 2 && !KVI8 && OTFM != kOtfQK;
 }
 template <int D, int QB, bool KVI8, int OTFM>
 constexpr int attn_waves_per_simd() {

@@ -244,14 +244,15 @@ def test_noalloc_entry_point_host_checks(tm):
 # per item keeps K's quantisation between two barriers beside three q-blocks: at
 # d = 128 (also in the kernel for partial head chunks), and at d = 64 in the
 # kernel for partial head chunks, whose three item bodies share the 168 VGPRs
-# of three waves per SIMD.  And the d = 128 two-head kernel in the bench's operand
-# mode, built for three waves per SIMD (measured faster with its spills).
+# of three waves per SIMD.  And the d = 128 two-head kernels with a single V
+# stage, built for three waves per SIMD (measured faster with their spills).
 SPILL_ALLOWANCE = {"_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2,
                    "_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2,
                    "_ZN7tilemix25attn_prefill_mixed_kernelILi64ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 8,
                    # two q-blocks at d = 128 with a single V stage, at 3 waves per SIMD (168 VGPRs)
-                   "_ZN7tilemix19attn_prefill_kernelILi128ELi2ELb0ELi2ELb0EEEvNS_8AttnArgsE": 3,
-                   "_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi2ELb0ELi2ELb0EEEvNS_8AttnArgsE": 3}
+                   "_ZN7tilemix19attn_prefill_kernelILi128ELi2ELb0ELi0ELb0EEEvNS_8AttnArgsE": 7,
+                   "_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi2ELb0ELi0ELb0EEEvNS_8AttnArgsE": 5,
+                   "_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi2ELb0ELi2ELb0EEEvNS_8AttnArgsE": 2}
 
 
 def test_kernel_resources_no_new_spills(tm):
