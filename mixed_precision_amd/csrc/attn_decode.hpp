@@ -31,8 +31,24 @@ void attn_decode_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char stA[A::KBYTES + A::VBYTES];
   __shared__ __attribute__((aligned(1024))) char stB[A::KBYTES + A::VBYTES];
 
-  const int b = (int)(blockIdx.x / a.Hk);
-  const int hk = (int)(blockIdx.x % a.Hk);
+  // Workgroups are dealt round-robin to the 8 XCDs.  Each XCD takes a
+  // contiguous range of the (sequence, KV head) pairs, ordered as the cache is
+  // (a sequence's heads together for a token-major cache, a head's sequences
+  // together for a head-major one), so that its L2 and address translation
+  // cover one compact slice of the cache.
+  int b, hk;
+  {
+    const int total = (int)gridDim.x, x = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
+    const int q = total >> 3, r = total & 7;
+    const int w = x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+    if (a.kv_sh > a.kv_st) {
+      hk = w / a.batch;
+      b = w - hk * a.batch;
+    } else {
+      b = w / a.Hk;
+      hk = w - b * a.Hk;
+    }
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);   // 16-key slice of every tile
