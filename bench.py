@@ -108,6 +108,8 @@ def work_model(w, words):
     d = w.head_dim
     G = w.num_q_heads // w.num_kv_heads
     pairs16 = pairs8 = 0
+    visits8 = 0            # (query tile, KV head, INT8 key tile) visits
+    tiles8 = set()         # distinct INT8 key tiles (sequence, KV head, key tile)
     for b, L in enumerate(w.lengths):
         L = int(L)
         Tb = (L + 63) // 64
@@ -116,9 +118,12 @@ def work_model(w, words):
             for hk in range(w.num_kv_heads):
                 word = int(words[hk, b, m])
                 n_full = m                                   # key tiles 0..m-1 are fully legal
-                full8 = sum(((word >> (n // w.g)) & 1) for n in range(n_full))
+                bits = [(word >> (n // w.g)) & 1 for n in range(m + 1)]
+                full8 = sum(bits[:n_full])
                 diag = rows * (rows + 1) // 2
-                dbit = (word >> (m // w.g)) & 1
+                dbit = bits[m]
+                visits8 += full8 + dbit
+                tiles8.update((b, hk, n) for n in range(m + 1) if bits[n])
                 p8 = full8 * 64 * rows + (diag if dbit else 0)
                 p16 = (n_full - full8) * 64 * rows + (0 if dbit else diag)
                 pairs8 += G * p8
@@ -128,7 +133,7 @@ def work_model(w, words):
     f_pv = 2 * d * (pairs16 + pairs8)
     t_star = f_qk16 / P_FP16 + f_qk8 / P_INT8 + f_pv / P_FP16
     return dict(pairs=pairs16 + pairs8, pairs_int8=pairs8, f_qk16=f_qk16, f_qk8=f_qk8, f_pv=f_pv,
-                ops=f_qk16 + f_qk8 + f_pv, t_star=t_star)
+                ops=f_qk16 + f_qk8 + f_pv, t_star=t_star, visits8=visits8, tiles8=len(tiles8))
 
 
 def _sampled_rows(inp, total_work, budget_s, seed=0):
@@ -601,9 +606,67 @@ def main():
         "hip_graph": bool(args.graph), "ms_per_step_eager": eager_ms,
         "settle": settle,
     }
+    if mode == 1:
+        res["config"]["k_quant_on_chip"] = k_quant_cost(args, w, tm, dev, q, k, v, cu, words, work,
+                                                        float(np.mean(attn_ms)))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(res), flush=True)
+
+
+def k_quant_cost(args, w, tm, dev, q, k, v, cu, words, work, attn_ms_otf):
+    """Where on-the-fly K goes: the same attention with K quantised once
+    beforehand (Q's operands still made in the kernel), timed in this process,
+    and the extra time per on-chip quantisation of an INT8 key tile.  Each
+    work item (query tile, KV head, chunk of up to three query heads) quantises
+    every INT8 key tile it visits, between two barriers of its workgroup."""
+    import torch
+    B, Hq, Hk, d = len(w.lengths), w.num_q_heads, w.num_kv_heads, w.head_dim
+    N = q.shape[0]
+    plan = tm.AttnPlan(tm.AttnProblem(B, w.max_seqlen, Hq, Hk, d, w.g, w.blk_q, w.sm_scale, w.kv_int8, False, 2),
+                       dev)
+    k_q = torch.empty((N, Hk, d), dtype=torch.int8, device=dev)
+    k_s = torch.empty((Hk, B, w.T), dtype=torch.float32, device=dev)
+    out = torch.empty((N, Hq, d), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    plan.schedule(cu, stream=stream)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tm.tilemix_quantize_blockwise(k, cu, w.max_seqlen, 64, k_q, k_s, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        plan.run_planned(q, k, v, None, None, k_q, k_s, cu, words, out, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    settle_clocks(step, args.settle_ms)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    kq_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
+    once_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
+    G = Hq // Hk
+    chunks = -(-G // 3)                               # fp16 K/V: up to three query heads per item
+    heads = -(-G // chunks)
+    quants = work["visits8"] * chunks
+    # resident workgroups (four waves each): the kernel's waves per SIMD times the CUs
+    waves = 2 if d == 128 else (3 if heads == 3 else 4)
+    slots = waves * torch.cuda.get_device_properties(dev).multi_processor_count
+    extra = attn_ms_otf - once_ms
+    return {"int8_tile_quantisations": quants, "distinct_int8_tiles": work["tiles8"],
+            "repeats_per_tile": quants / max(work["tiles8"], 1),
+            "attn_ms_k_quantised_once": once_ms, "k_quantiser_pass_ms": kq_ms,
+            "attn_ms_extra": extra,
+            "us_per_tile_quantisation_per_workgroup": extra * 1e3 * slots / max(quants, 1),
+            "concurrent_workgroups": slots,
+            "note": "attention with K quantised once (and its quantiser pass) timed in the same process; "
+                    "extra time spread over the concurrent workgroups"}
 
 
 if __name__ == "__main__":
