@@ -240,14 +240,13 @@ def test_noalloc_entry_point_host_checks(tm):
     assert tm.tilemix_attn_workspace_size(_params(tm, batch=480)) <= 4 << 20 < need
 
 
-# Known spills of non-debug kernels (VGPRs): the full on-the-fly mode with 3 heads
-# per item keeps K's quantisation between two barriers beside three q-blocks: at
-# d = 128 (also in the kernel for partial head chunks), and at d = 64 in the
-# kernel for partial head chunks, whose three item bodies share the 168 VGPRs
-# of three waves per SIMD.  And the d = 128 two-head kernels with a single V
-# stage, built for three waves per SIMD (measured faster with their spills).
-SPILL_ALLOWANCE = {"_ZN7tilemix19attn_prefill_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2,
-                   "_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 2,
+# Known spills of non-debug kernels (VGPRs), at their current counts: the full
+# on-the-fly mode with 3 heads per item keeps K's quantisation between two
+# barriers beside three q-blocks, in the kernels for partial head chunks at
+# d = 128 and at d = 64 (whose three item bodies share the 168 VGPRs of three
+# waves per SIMD).  And the d = 128 two-head kernels with a single V stage,
+# built for three waves per SIMD (measured faster with their spills).
+SPILL_ALLOWANCE = {"_ZN7tilemix25attn_prefill_mixed_kernelILi128ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 1,
                    "_ZN7tilemix25attn_prefill_mixed_kernelILi64ELi3ELb0ELi1ELb0EEEvNS_8AttnArgsE": 8,
                    # two q-blocks at d = 128 with a single V stage, at 3 waves per SIMD (168 VGPRs)
                    "_ZN7tilemix19attn_prefill_kernelILi128ELi2ELb0ELi0ELb0EEEvNS_8AttnArgsE": 7,
