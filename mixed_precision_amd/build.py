@@ -4,7 +4,9 @@ Every HIP/C++ source under csrc/ is compiled to an object in parallel and the
 objects are linked into ``mixed_precision_amd/libtilemix.so``.  Always rebuilds
 (the caller decides when); objects go to ``mixed_precision_amd/_build``.  The
 compiler's per-kernel resource figures (VGPRs, spills, scratch, occupancy,
-LDS) are kept in ``mixed_precision_amd/kernel_resources.json``.
+LDS) are kept in ``mixed_precision_amd/kernel_resources.json``.  The
+microbenchmarks under probe/ become ``libtilemix_probe.so`` (not part of the
+attention path).
 """
 from __future__ import annotations
 
@@ -23,6 +25,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtilemix.so")
+PROBE_DIR = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libtilemix_probe.so")
 
 ARCH = os.environ.get("TILEMIX_ARCH", "gfx950")
 
@@ -79,26 +83,34 @@ def _compile(src: str):
     return obj, _resources(r.stderr)
 
 
+def _link(objs, out: str):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = True, jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)), 16)
+    probe_srcs = sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip")))
+    jobs = jobs or min(len(srcs) + len(probe_srcs), max(1, (os.cpu_count() or 4)), 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        probe_done = ex.map(_compile, probe_srcs)
         done = list(ex.map(_compile, srcs))
+        probe_objs = [o for o, _ in probe_done]
     objs = [o for o, _ in done]
     res = {}
     for _, r in done:
         res.update(r)
     with open(RESOURCES, "w") as f:
         json.dump(res, f, indent=1, sort_keys=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    _link(objs, LIB)
+    _link(probe_objs, PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
+        print(f"built {LIB} from {len(srcs)} sources (and {os.path.basename(PROBE_LIB)})", file=sys.stderr)
     return LIB
 
 

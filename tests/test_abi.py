@@ -49,6 +49,19 @@ def test_library_exports_every_declared_symbol(tm):
         getattr(tm.lib(), n)
 
 
+def test_probe_library_exports_its_header():
+    """The microbenchmark library (not part of the attention path) exports
+    what include/tilemix_probe.h declares."""
+    probe_lib = os.path.join(ROOT, "mixed_precision_amd", "libtilemix_probe.so")
+    if not os.path.exists(probe_lib):
+        from mixed_precision_amd import build as b
+        b.build(verbose=False)
+    src = open(os.path.join(ROOT, "include", "tilemix_probe.h")).read()
+    declared = set(re.findall(r"\b(tilemix_\w+)\s*\(", src))
+    out = subprocess.run(["nm", "-D", "--defined-only", probe_lib], capture_output=True, text=True, check=True).stdout
+    assert declared and declared <= set(re.findall(r"\bT (tilemix_\w+)", out))
+
+
 def test_status_strings(tm):
     for code, name in tm.STATUS_NAMES.items():
         assert tm.lib().tilemix_status_string(code).decode() == name
