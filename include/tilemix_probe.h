@@ -24,7 +24,9 @@ enum {
   TILEMIX_PROBE_MFMA_I8 = 4,     /* 16 v_mfma_i32_16x16x64_i8 per iteration, 4 accumulators */
   TILEMIX_PROBE_MFMA32_F16 = 5,  /* 16 v_mfma_f32_32x32x16_f16 per iteration, 4 accumulators */
   TILEMIX_PROBE_LDS128 = 6,      /* 8 ds_read_b128 per iteration, 16 contiguous bytes per lane */
-  TILEMIX_PROBE_LDS_TR16 = 7     /* 8 ds_read_b64_tr_b16 per iteration, the attention kernel's V^T addressing */
+  TILEMIX_PROBE_LDS_TR16 = 7,    /* 8 ds_read_b64_tr_b16 per iteration, the attention kernel's V^T addressing */
+  TILEMIX_PROBE_MIX = 8          /* 16 v_mfma_f32_16x16x32_f16 and 32 v_fma_f32 per iteration, one wave,
+                                    each MFMA followed by two independent FMAs */
 };
 
 /* Launches num_workgroups (1..65536) workgroups of 8 waves, one per CU (80 KB
@@ -32,7 +34,8 @@ enum {
  * (wave w + 4 on the SIMD of wave w) run op_b for iters_b, after a common
  * barrier.  Supported pairs: (FMA, IDLE), (FMA, FMA), (EXP, IDLE), (EXP, EXP),
  * (MFMA_F16, IDLE), (MFMA_F16, MFMA_F16), (MFMA_I8, IDLE), (MFMA32_F16, IDLE),
- * (MFMA_F16, FMA), (MFMA_I8, FMA), (MFMA32_F16, FMA) and each LDS stream with
+ * (MFMA_F16, FMA), (MFMA_I8, FMA), (MFMA32_F16, FMA), (MIX, IDLE), (MIX, MIX)
+ * and each LDS stream with
  * itself.
  *   stamps: device, uint64 [num_workgroups * 8][2], caller-owned: each wave's
  *           shader-clock stamps (s_memtime) before and after its loop;

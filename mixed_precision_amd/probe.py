@@ -8,6 +8,11 @@ co-running wave's FMA stream, and the LDS bytes a CU reads per cycle.  Cycles
 are those of the s_memtime counter; the run also reports that counter's rate
 against host time.
 
+The mixed stream: one wave issues 16 MFMAs and 32 independent FMAs per
+iteration, one MFMA then two FMAs; compared with the MFMA-only and FMA-only
+times of the same counts it shows how much VALU work hides under a wave's own
+MFMAs.
+
 The MFMA cost to the port: waves 0-3 stream MFMAs while waves 4-7 (one per
 SIMD beside them) stream F FMAs.  The MFMA stream is sized to outlast the FMA
 stream; the MFMAs issued inside the FMA window are its count minus those
@@ -26,7 +31,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libtilemix_probe.so")
 
-IDLE, FMA, EXP, MFMA_F16, MFMA_I8, MFMA32_F16, LDS128, LDS_TR16 = range(8)
+IDLE, FMA, EXP, MFMA_F16, MFMA_I8, MFMA32_F16, LDS128, LDS_TR16, MIX = range(9)
 PER_ITER = {FMA: 32, EXP: 32, MFMA_F16: 16, MFMA_I8: 16, MFMA32_F16: 16, LDS128: 8, LDS_TR16: 8}
 LDS_BYTES_PER_LANE = {LDS128: 16, LDS_TR16: 8}
 
@@ -88,6 +93,14 @@ def measure(p: Probe, iters: int = 2048) -> dict:
         if op == MFMA_F16:
             out["counter_per_ns"] = a / (ms * 1e6)       # s_memtime ticks per ns of host time
     c_fma = out["fma"]["cycles_alone"]
+    # one wave's own MFMAs and FMAs interleaved (16 + 32 per iteration): how much
+    # of the FMA time hides under the MFMAs, alone and with two such waves per SIMD
+    t_m, t_f = 16 * out["mfma_f16_16x16x32"]["cycles_alone"], 32 * c_fma
+    a, _, _, _ = p.run(MIX, IDLE, iters, 0)
+    _, _, span, _ = p.run(MIX, MIX, iters, iters)
+    out["mix_mfma_fma"] = {"cycles_per_iteration_alone": a / iters, "mfma_only": t_m, "fma_only": t_f,
+                           "fma_hidden_fraction": (t_m + t_f - a / iters) / t_f,
+                           "simd_cycles_per_iteration_two_waves": span / (2 * iters)}
     # MFMA cost to a co-running wave's FMA issue
     f_iters = iters
     for name, op in (("mfma_f16_16x16x32", MFMA_F16), ("mfma_i8_16x16x64", MFMA_I8),

@@ -13,6 +13,8 @@
 //   MFMA_F16  16 v_mfma_f32_16x16x32_f16 into 4 independent accumulators
 //   MFMA_I8   16 v_mfma_i32_16x16x64_i8, 4 accumulators
 //   MFMA32    16 v_mfma_f32_32x32x16_f16, 4 accumulators
+//   MIX       16 v_mfma_f32_16x16x32_f16 and 32 v_fma_f32 of one wave, one MFMA
+//             then two FMAs
 //   LDS128 / LDSTR16: 8 ds_read_b128 / ds_read_b64_tr_b16, each lane's
 //   address inside the 64 KB probe area (a contiguous 16-byte slot per lane;
 //   the transposed reads use the attention kernel's V^T addressing over
@@ -103,6 +105,35 @@ __device__ __forceinline__ float stream(int iters, const char* lds, int lane, in
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) r += acc[k][0] + acc[k][15];
+  } else if constexpr (OP == TILEMIX_PROBE_MIX) {
+    // one wave's own MFMAs and FMAs, interleaved one MFMA to two FMAs
+    const f16x8 a = {(f16)1.0f, (f16)0.5f, (f16)0.25f, (f16)0.125f, (f16)1.0f, (f16)0.5f, (f16)0.25f, (f16)0.125f};
+    const f16x8 b = {(f16)1e-3f, (f16)1e-3f, (f16)1e-3f, (f16)1e-3f, (f16)1e-3f, (f16)1e-3f, (f16)1e-3f, (f16)1e-3f};
+    const float fa = 0.999f - (float)lane * 1e-7f, fb = 1e-3f + (float)lane * 1e-7f;
+    f32x4 acc[4] = {};
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = (float)lane * 1e-3f + (float)k;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[k], 0, 0, 0);
+          x[2 * k] = __builtin_fmaf(x[2 * k], fa, fb);
+          x[2 * k + 1] = __builtin_fmaf(x[2 * k + 1], fa, fb);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r += acc[k][0] + acc[k][3];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r += x[k];
   } else if constexpr (OP == TILEMIX_PROBE_LDS128) {
     u32x4 acc = {0, 0, 0, 0};
     const int base = wave * 8192 + lane * 16;
@@ -115,13 +146,15 @@ __device__ __forceinline__ float stream(int iters, const char* lds, int lane, in
   } else if constexpr (OP == TILEMIX_PROBE_LDS_TR16) {
     // the attention kernel's V^T read: 16-lane group gq reads keys 4gq .. 4gq+3
     // (one 1056-byte block each), 32 bytes of channels per key
+    // (the 8 addresses are loop-invariant: the LDS has no cache, so reading
+    // them again costs the same, and no address arithmetic enters the loop)
     const int gq = lane >> 4, jl = lane & 15;
-    const int base = (4 * gq + (jl >> 2)) * 1056 + 8 * (jl & 3);
+    const int base = (4 * gq + (jl >> 2)) * 1056 + 8 * (jl & 3) + (wave & 1) * 16 * 1056;
     s16x4 acc = {0, 0, 0, 0};
     for (int i = 0; i < iters; ++i) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int off = (base + ((wave * 8 + u) & 15) * 64 + (i & 7) * 16 * 1056) & (kArea - 1);
+        const int off = base + u * 64;   // channel blocks of one key group, as P.V reads them
         acc ^= __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off));
       }
     }
@@ -177,6 +210,8 @@ extern "C" int tilemix_probe_run(int op_a, int op_b, int iters_a, int iters_b, i
   TM_PROBE_CASE(TILEMIX_PROBE_MFMA_F16, TILEMIX_PROBE_FMA)
   TM_PROBE_CASE(TILEMIX_PROBE_MFMA_I8, TILEMIX_PROBE_FMA)
   TM_PROBE_CASE(TILEMIX_PROBE_MFMA32_F16, TILEMIX_PROBE_FMA)
+  TM_PROBE_CASE(TILEMIX_PROBE_MIX, TILEMIX_PROBE_IDLE)
+  TM_PROBE_CASE(TILEMIX_PROBE_MIX, TILEMIX_PROBE_MIX)
   TM_PROBE_CASE(TILEMIX_PROBE_LDS128, TILEMIX_PROBE_LDS128)
   TM_PROBE_CASE(TILEMIX_PROBE_LDS_TR16, TILEMIX_PROBE_LDS_TR16)
 #undef TM_PROBE_CASE
