@@ -52,14 +52,27 @@ def kernel_source_digest():
     return source_digest(KERNEL_SOURCES)
 
 
+def build_flags_text():
+    """What the build script decides about the kernels' code: the target, the
+    compile flags (without the absolute include paths, which differ between
+    checkouts) and the per-source flags."""
+    from mixed_precision_amd import build as b
+    flags = [f for f in b.CXXFLAGS if not os.path.isabs(f)]
+    return json.dumps({"arch": b.ARCH, "flags": flags, "source_flags": b.SOURCE_FLAGS}, sort_keys=True).encode()
+
+
 def source_digest(files):
     """sha256 over sources: C++ files without their // comments and blank lines
     (an edit of a comment leaves the code, and so the counters taken on it,
-    valid), Python files as they are."""
+    valid), the build script by its compile flags alone, other Python files as
+    they are."""
     import hashlib
     import re
     h = hashlib.sha256()
     for rel in files:
+        if rel.endswith("build.py"):
+            h.update(build_flags_text())
+            continue
         with open(os.path.join(ROOT, rel), "rb") as f:
             data = f.read()
         if not rel.endswith(".py"):
