@@ -1,7 +1,8 @@
-"""CPU checks of the benchmark's work model: the legal (query, key) pairs per
-path that set the blended MFMA roofline, and the INT8 tile visits that the
-on-the-fly line reports, against brute force over every pair of a small ragged
-GQA batch with route words from the oracle's packer."""
+"""CPU checks of the benchmark's work models: the legal (query, key) pairs per
+path that set the blended MFMA roofline (prefill, and chunked prefill / decode),
+and the INT8 tile visits that the on-the-fly line reports, against brute force
+over every pair of small ragged GQA batches with route words from the oracle's
+packer."""
 import numpy as np
 import pytest
 
@@ -37,9 +38,36 @@ def test_work_model_matches_brute_force(g, p):
     d = w.head_dim
     assert got["f_qk8"] == 2 * d * pairs8 and got["f_qk16"] == 2 * d * pairs16
     assert got["f_pv"] == 2 * d * (pairs8 + pairs16)
-    t_star = 2 * d * pairs16 / bench.P_FP16 + 2 * d * pairs8 / bench.P_INT8 + 2 * d * (pairs8 + pairs16) / bench.P_FP16
+    t_star = (2 * d * pairs16 / bench.P_FP16 + 2 * d * pairs8 / bench.P_INT8 +
+              2 * d * (pairs8 + pairs16) / bench.P_FP16)
     assert got["t_star"] == pytest.approx(t_star, rel=1e-12)
     if p == 0.0:
         assert pairs8 == 0 and visits8 == 0
     if p == 1.0:
         assert pairs16 == 0
+
+
+@pytest.mark.parametrize("g", [1, 2])
+def test_chunked_work_model_matches_brute_force(g):
+    """Chunked prefill and decode: the queries are the last Lq of Lk positions
+    (key j legal for query i iff j <= Lk - Lq + i); pairs per path against
+    every pair, including one-query rows and chunks that start inside a tile."""
+    from workloads.synth import make_chunked_workload
+    w = make_chunked_workload(620 + g, lengths_q=[130, 1, 64, 7], lengths_k=[300, 200, 64, 70], num_q_heads=4,
+                              num_kv_heads=2, head_dim=64, g=g, p=0.6)
+    words = build_route_mask(w.tile_route, w.cu_seqlens, w.max_seqlen, g, w.cu_seqlens_k, w.max_seqlen_k)
+    G = w.num_q_heads // w.num_kv_heads
+    pairs8 = pairs16 = 0
+    for b, (Lq, Lk) in enumerate(zip(w.lengths, w.lengths_k)):
+        for hk in range(w.num_kv_heads):
+            for i in range(Lq):
+                for j in range(Lk - Lq + i + 1):
+                    if route_bit(words[hk, b, i // 64], j // 64, g):
+                        pairs8 += G
+                    else:
+                        pairs16 += G
+    got = bench.chunked_work(w, words)
+    assert got["pairs_int8"] == pairs8 and got["pairs"] == pairs8 + pairs16
+    d = w.head_dim
+    assert got["t_star"] == pytest.approx(2 * d * pairs16 / bench.P_FP16 + 2 * d * pairs8 / bench.P_INT8 +
+                                          2 * d * (pairs8 + pairs16) / bench.P_FP16, rel=1e-12)
