@@ -692,6 +692,70 @@ def test_attn_chunked_full(gp, case):
             assert mo <= MAX_ABS and ro <= REL_FRO
 
 
+
+def _random_case(seed):
+    """A seeded random configuration inside the supported range: 1-4 sequences
+    with lengths at tile edges or random (1..400), prefill or chunked prefill /
+    decode, d 64 or 128, 1-3 KV heads and 1-8 or 16 query heads per KV head,
+    g 1-4, INT8 coverage 0-100 %, fp16 or INT8 cache, blk_q 64 or 128, with
+    or without outlier channels."""
+    import random
+    rng = random.Random(seed)
+    d = rng.choice([64, 128])
+    hk = rng.choice([1, 2, 3])
+    hq = hk * rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 16])
+    kv8 = rng.random() < 0.35
+    blk_q = rng.choice([64, 64, 128])
+    p = rng.choice([0.0, 0.3, 0.5, 0.8, 1.0])
+    outl = rng.random() < 0.6
+    chunked = rng.random() < 0.3
+    nseq = rng.randint(1, 4)
+
+    def pick():
+        return rng.choice([1, 2, 63, 64, 65, 127, 128, 129, rng.randint(1, 400)])
+
+    if chunked:
+        lk = [pick() + rng.choice([0, 64, 200]) for _ in range(nseq)]
+        lq = [rng.choice([1, min(k, rng.randint(1, k))]) for k in lk]
+        g = rng.choice([1, 2, 3])
+        w = make_chunked_workload(seed, lengths_q=lq, lengths_k=lk, num_q_heads=hq, num_kv_heads=hk, head_dim=d,
+                                  g=g, p=p, outliers=outl, kv_int8=kv8, blk_q=blk_q)
+        desc = f"chunked lq={lq} lk={lk}"
+    else:
+        lens = [pick() for _ in range(nseq)]
+        g = rng.choice([1, 2, 3, 4])
+        w = make_workload(seed, lengths=lens, num_q_heads=hq, num_kv_heads=hk, head_dim=d, g=g, p=p,
+                          outliers=outl, kv_int8=kv8, blk_q=blk_q)
+        desc = f"prefill lengths={lens}"
+    return w, f"{desc} heads {hq}/{hk} d={d} g={g} p={p} kv_int8={kv8} blk_q={blk_q} outliers={outl}"
+
+
+@pytest.mark.parametrize("seed", list(range(9000, 9024)))
+def test_attn_random_configs(gp, seed):
+    """Seeded random configurations (`_random_case`) against the oracle, every
+    element; for an fp16 cache also with the operands made in the kernel (the
+    same bits, or within the bar where decode goes to the decode kernel)."""
+    import torch
+    w, desc = _random_case(seed)
+    _announce(f"attn random {seed}: {desc}")
+    t = gp.prepare(w)
+    out = gp.attn(w, t)
+    modes = [] if w.kv_int8 else [gp.attn(w, t, otf=True), gp.attn(w, t, otf=2)]
+    torch.cuda.synchronize()
+    ref = orc.attn_prefill(oracle_inputs(w))
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    ma, rf = gp.errors(got, ref)
+    print(f"  max_abs={ma:.3e} rel_fro={rf:.3e}")
+    assert ma <= MAX_ABS and rf <= REL_FRO
+    decode = w.cu_seqlens_k is not None and max(w.lengths) == 1
+    for o in modes:
+        if decode:   # decode kernel against the prefill kernel: another order
+            mo, ro = gp.errors(o.cpu().numpy(), ref)
+            assert mo <= MAX_ABS and ro <= REL_FRO
+        else:
+            assert torch.equal(o, out)
+
 def test_attn_chunk_rows_equal_prefill_rows(gp):
     """A chunk that starts on a Q block sees the same keys, scales and routes in
     the same order as the same rows of the full prefill, so the HIP path gives
